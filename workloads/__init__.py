@@ -1,0 +1,181 @@
+"""Seeded synthetic inputs for windowed int8 paged prefill attention.
+
+This module only draws random numbers and lays them out; it holds none of the
+attention arithmetic, so both the CPU oracle and the HIP path can take their
+inputs from it without sharing any of the method.
+
+The pages ("perf(qwen35): int8 tensor-core prefill attention for Qwythos",
+sections "Summary" and "Why the attention, and why tensor cores") measure
+whole-model prefill of a 9B model on held-out prompts.  Neither the weights nor
+the prompts exist here, so seeded tensors with the pages' shapes stand in for
+them: head_dim 256, GQA-4, 16-token int8 KV pages with per-token scales, a
+default window of 256 blocks plus one sink block, contexts 4k / 32k / 64k.
+
+Layouts (all host numpy arrays, C-contiguous):
+  q_bf16      uint16 [n_tokens][n_q_heads][256]   bf16 bit patterns
+  q_f32       float32 same shape, the exact widening of q_bf16
+  k_pool      int8   [n_pool_pages][16][n_kv_heads][256]
+  v_pool      int8   same
+  k_scale     float32 [n_pool_pages][16][n_kv_heads]
+  v_scale     float32 same
+  page_table  int32  [ceil(n_tokens / 16)]  logical block -> physical page
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+
+HEAD_DIM = 256
+PAGE = 16
+
+__all__ = ["Case", "CONFIGS", "make_config", "make_case", "HEAD_DIM", "PAGE"]
+
+
+@dataclasses.dataclass
+class Case:
+    name: str
+    n_tokens: int
+    n_q_heads: int
+    n_kv_heads: int
+    window_blocks: int
+    sink_blocks: int
+    softmax_scale: float
+    out_dtype: str            # "f32" or "bf16"
+    q_bf16: np.ndarray
+    q_f32: np.ndarray
+    k_pool: np.ndarray
+    v_pool: np.ndarray
+    k_scale: np.ndarray
+    v_scale: np.ndarray
+    page_table: np.ndarray
+    seed: int
+
+    @property
+    def n_pool_pages(self) -> int:
+        return int(self.k_pool.shape[0])
+
+    @property
+    def n_blocks(self) -> int:
+        return (self.n_tokens + PAGE - 1) // PAGE
+
+
+def _round_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 bit patterns, round-half-to-even (input generation only)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32)
+    bias = ((u >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
+    return ((u + bias) >> np.uint32(16)).astype(np.uint16)
+
+
+def _bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def make_case(
+    *,
+    n_tokens: int,
+    n_q_heads: int,
+    n_kv_heads: int,
+    window_blocks: int,
+    sink_blocks: int,
+    seed: int,
+    name: str = "custom",
+    softmax_scale: float = 1.0 / 16.0,
+    out_dtype: str = "bf16",
+    scale_lo: float = 0.005,
+    scale_hi: float = 0.02,
+    log_uniform_scales: bool = False,
+    extra_pool_frac: float = 0.0,
+    q_outlier_frac: float = 0.0,
+    k_saturated_frac: float = 0.0,
+    poison_unused: bool = True,
+) -> Case:
+    """Draw one seeded case.
+
+    Draw order is fixed: Q, K, V, k_scale, v_scale, page permutation, then the
+    outlier selections (Q outlier rows/channels, saturated K tokens, signs).
+    Unused pool slots (pages not in the table, and the tail slots of a partial
+    last page) get NaN scales, so any stray read of them poisons the output.
+    """
+    if n_q_heads % n_kv_heads:
+        raise ValueError("n_q_heads must be a multiple of n_kv_heads")
+    rng = np.random.default_rng(seed)
+    n_blocks = (n_tokens + PAGE - 1) // PAGE
+    n_pool = n_blocks + int(round(extra_pool_frac * n_blocks))
+
+    q = rng.standard_normal((n_tokens, n_q_heads, HEAD_DIM), dtype=np.float32)
+    k_pool = rng.integers(-127, 128, size=(n_pool, PAGE, n_kv_heads, HEAD_DIM), dtype=np.int8)
+    v_pool = rng.integers(-127, 128, size=(n_pool, PAGE, n_kv_heads, HEAD_DIM), dtype=np.int8)
+    if log_uniform_scales:
+        lo, hi = math.log(scale_lo), math.log(scale_hi)
+        k_scale = np.exp(rng.uniform(lo, hi, size=(n_pool, PAGE, n_kv_heads))).astype(np.float32)
+        v_scale = np.exp(rng.uniform(lo, hi, size=(n_pool, PAGE, n_kv_heads))).astype(np.float32)
+    else:
+        k_scale = rng.uniform(scale_lo, scale_hi, size=(n_pool, PAGE, n_kv_heads)).astype(np.float32)
+        v_scale = rng.uniform(scale_lo, scale_hi, size=(n_pool, PAGE, n_kv_heads)).astype(np.float32)
+    perm = rng.permutation(n_pool).astype(np.int32)
+    page_table = np.ascontiguousarray(perm[:n_blocks])
+
+    if q_outlier_frac > 0.0:
+        n_rows = n_tokens * n_q_heads
+        n_out = int(math.ceil(q_outlier_frac * n_rows))
+        rows = rng.choice(n_rows, size=n_out, replace=False)
+        qf = q.reshape(n_rows, HEAD_DIM)
+        for r in rows:
+            ch = rng.choice(HEAD_DIM, size=4, replace=False)
+            qf[r, ch] *= 30.0
+    if k_saturated_frac > 0.0:
+        n_sat = int(math.ceil(k_saturated_frac * n_tokens))
+        toks = rng.choice(n_tokens, size=n_sat, replace=False)
+        signs = rng.integers(0, 2, size=(n_sat, n_kv_heads, HEAD_DIM), dtype=np.int8)
+        vals = np.where(signs == 1, np.int8(127), np.int8(-127)).astype(np.int8)
+        for i, t in enumerate(toks):
+            k_pool[page_table[t // PAGE], t % PAGE] = vals[i]
+
+    if poison_unused:
+        used = np.zeros(n_pool, dtype=bool)
+        used[page_table] = True
+        k_scale[~used] = np.nan
+        v_scale[~used] = np.nan
+        tail = n_blocks * PAGE - n_tokens
+        if tail:
+            last = page_table[n_blocks - 1]
+            k_scale[last, PAGE - tail:] = np.nan
+            v_scale[last, PAGE - tail:] = np.nan
+
+    q_bits = _round_to_bf16_bits(q)
+    return Case(
+        name=name, n_tokens=n_tokens, n_q_heads=n_q_heads, n_kv_heads=n_kv_heads,
+        window_blocks=window_blocks, sink_blocks=sink_blocks,
+        softmax_scale=float(softmax_scale), out_dtype=out_dtype,
+        q_bf16=q_bits, q_f32=_bf16_bits_to_f32(q_bits),
+        k_pool=k_pool, v_pool=v_pool, k_scale=k_scale, v_scale=v_scale,
+        page_table=page_table, seed=seed,
+    )
+
+
+# The five seeded workloads.  Sizes, heads, window, distributions and pool
+# shapes follow the pages' shapes (hd256, GQA-4, 16-token pages, window 256
+# blocks, contexts 4k/32k/64k) plus a full-causal outlier stress case.
+CONFIGS = {
+    "tiny": dict(n_tokens=64, n_q_heads=2, n_kv_heads=1, window_blocks=0, sink_blocks=0,
+                 seed=1001, out_dtype="f32"),
+    "4k": dict(n_tokens=4096, n_q_heads=16, n_kv_heads=4, window_blocks=256, sink_blocks=1,
+               seed=1002),
+    "32k": dict(n_tokens=32768, n_q_heads=16, n_kv_heads=4, window_blocks=256, sink_blocks=1,
+                seed=1003),
+    "64k": dict(n_tokens=65536, n_q_heads=16, n_kv_heads=4, window_blocks=256, sink_blocks=1,
+                seed=1004, extra_pool_frac=0.25),
+    "16k_full": dict(n_tokens=16384, n_q_heads=32, n_kv_heads=8, window_blocks=0, sink_blocks=0,
+                     seed=1005, scale_lo=1e-3, scale_hi=5e-2, log_uniform_scales=True,
+                     q_outlier_frac=0.01, k_saturated_frac=0.02),
+}
+
+
+def make_config(name: str, seed: int | None = None) -> Case:
+    kw = dict(CONFIGS[name])
+    if seed is not None:
+        kw["seed"] = seed
+    return make_case(name=name, **kw)
