@@ -1,0 +1,192 @@
+"""Benchmark: int8 TOPS of windowed int8 paged prefill attention (hd256) at 32k.
+
+One step = the whole path on one batch of synthetic input already resident in
+HBM: Q row quantization, the attention kernel, and the attended-key counts.
+Throughput counts 4 * sum_t |A(t)| * 256 * n_q_heads int8 ops per step (the
+QK^T and PV multiply-adds of every attended (row, key) pair).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 32k]
+                    [--no-cpu-baseline] [--cpu-seconds S] [--copy-calibration]
+
+Prints one JSON line.  Runs on one GPU only.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "int8 TOPS & % of MI355X int8 MFMA peak, hd256 windowed prefill attn at 32k"
+PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 matrix peak, 5.0 POP/s
+HBM_PEAK_GBS = 8000.0
+ATTN_KERNEL_SOURCES = ["windowed_int8_paged_amd/csrc/wpa_attn.hip", "windowed_int8_paged_amd/csrc/wpa_common.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_prefill_attn_32k.json")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in ATTN_KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, p), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def workload_desc(case) -> str:
+    win = (f"window {case.window_blocks} blocks + {case.sink_blocks} sink block(s)"
+           if case.window_blocks > 0 else "full causal")
+    return (f"hd256 prefill attention, N={case.n_tokens}, {case.n_q_heads} q heads / "
+            f"{case.n_kv_heads} kv heads, {win}, int8 paged pool of {case.n_pool_pages} "
+            f"shuffled 16-token pages, bf16 Q and output")
+
+
+def copy_calibration(steps: int) -> None:
+    """A plain device copy of known size, for scaling rocprofv3 FETCH/WRITE_SIZE."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_per_direction": n, "launches": steps}), flush=True)
+
+
+def cpu_baseline(case, seconds: float):
+    """Time the oracle's int8 mirror (as it stands) on a bounded sample of tiles."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    n_tiles = (case.n_tokens + 15) // 16
+    first = min(n_tiles - 1, max(0, case.window_blocks + 1)) if case.window_blocks > 0 else n_tiles // 2
+    tiles, t0 = [], time.perf_counter()
+    tile = first
+    while True:
+        oracle.attention_int8_mirror(case, tiles=[tile])
+        tiles.append(tile)
+        tile = first + (tile - first + 7) % (n_tiles - first)
+        if time.perf_counter() - t0 >= seconds or len(tiles) >= n_tiles:
+            break
+    dt = time.perf_counter() - t0
+    rows = np.concatenate([oracle.tile_rows(case.n_tokens, t) for t in tiles])
+    counts = oracle.mask_counts(case.n_tokens, case.window_blocks, case.sink_blocks)[rows]
+    ops = 4.0 * counts.sum() * 256 * case.n_q_heads
+    return {
+        "value": ops / dt / 1e12, "unit": "TOPS", "cores": int(threads), "kind": "oracle",
+        "sample": f"int8-mirror oracle (numpy fp64) on {len(tiles)} of {n_tiles} query tiles "
+                  f"({len(rows)} rows x {case.n_q_heads} heads, {int(counts.sum())} attended keys/head) "
+                  f"of the same workload, {dt:.1f} s; host cpu_count {os.cpu_count()}",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="32k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this path has no multi-GPU mode "
+              "(sharding by KV head or by query range is described in the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    if args.copy_calibration:
+        copy_calibration(max(1, args.steps))
+        return
+
+    import windowed_int8_paged_amd as wpa
+    import workloads
+
+    case = workloads.make_config(args.config)
+    N, Hq = case.n_tokens, case.n_q_heads
+    print(f"[bench] config {args.config}: {workload_desc(case)}", file=sys.stderr, flush=True)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    q = torch.from_numpy(case.q_bf16.view(np.int16)).cuda().view(torch.bfloat16)
+    k_pool, v_pool = dev(case.k_pool), dev(case.v_pool)
+    k_scale, v_scale, page_table = dev(case.k_scale), dev(case.v_scale), dev(case.page_table)
+    q_i8 = torch.empty((N, Hq, 256), dtype=torch.int8, device="cuda")
+    q_scale = torch.empty((N, Hq), dtype=torch.float32, device="cuda")
+    out = torch.empty((N, Hq, 256), dtype=torch.bfloat16, device="cuda")
+    counts = torch.empty((N,), dtype=torch.int32, device="cuda")
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        wpa.quantize_q_rows(q, q_i8, q_scale)
+        if ev is not None:
+            ev[1].record()
+        wpa.prefill_attn_i8(q_i8, q_scale, k_pool, v_pool, k_scale, v_scale, page_table,
+                            case.window_blocks, case.sink_blocks, case.softmax_scale, out=out)
+        if ev is not None:
+            ev[2].record()
+        wpa.mask_counts(N, case.window_blocks, case.sink_blocks, counts=counts)
+        if ev is not None:
+            ev[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    total_keys = int(counts.to(torch.int64).sum().item())
+    ops = 4.0 * total_keys * 256 * Hq
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    quant_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    attn_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    mask_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+    ms_per_step = wall * 1e3 / args.steps
+    value = ops / (ms_per_step * 1e-3) / 1e12
+    attn_tops = ops / (attn_ms * 1e-3) / 1e12
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        t = json.load(open(TRAFFIC_FILE))
+        if t.get("kernel_source_hash") == kernel_source_hash() and t.get("config") == args.config:
+            traffic = t.get("hbm_bytes_per_launch")
+
+    res = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TOPS", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int8", "data": "synthetic",
+        "config": {"workload": workload_desc(case), "name": args.config, "n_tokens": N,
+                   "n_q_heads": Hq, "n_kv_heads": case.n_kv_heads, "head_dim": 256,
+                   "window_blocks": case.window_blocks, "sink_blocks": case.sink_blocks,
+                   "attended_keys": total_keys, "int8_ops_per_step": ops, "parallelism": "single-gpu"},
+        "pct_of_int8_peak_step": round(100 * value / PEAK_INT8_TOPS, 2),
+        "kernel_ms": {"quantize_q_rows": round(quant_ms, 4), "prefill_attn_i8": round(attn_ms, 4),
+                      "mask_counts": round(mask_ms, 4)},
+        "roofline": {"bound": "mfma", "achieved": round(attn_tops, 2), "peak": PEAK_INT8_TOPS,
+                     "unit": "TFLOP/s", "frac": round(attn_tops / PEAK_INT8_TOPS, 4),
+                     "traffic": traffic, "kernel": "prefill_attn_i8",
+                     "kernel_source_hash": kernel_source_hash()},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,136 @@
+/*
+ * wpa.h -- windowed int8 paged prefill attention for AMD Instinct MI355X (gfx950).
+ *
+ * One operation: causal prefill attention at head_dim 256 over a paged int8 KV
+ * pool, with a StreamingLLM sink + window block mask and grouped-query heads.
+ * Source of the method: the page "perf(qwen35): int8 tensor-core prefill
+ * attention for Qwythos" (sections "Why the attention, and why tensor cores"
+ * and "Relation to open PRs"), and for the window semantics the page
+ * "perf(qwen35): fp16 shared-memory tiles for windowed prefill attention"
+ * (sections "Summary", "Proof of speedup").
+ *
+ * Conventions shared by every entry point
+ *   - head_dim is fixed at 256 (WPA_HEAD_DIM); a KV page holds exactly 16
+ *     tokens (WPA_PAGE_TOKENS), the page being the block of the mask.
+ *   - All pointers are DEVICE pointers on the current HIP device.  The caller
+ *     allocates and frees every buffer; the library allocates nothing, keeps no
+ *     global state, never synchronizes, and is safe to call from several host
+ *     threads.  Work is enqueued on `stream` (0 = the legacy default stream)
+ *     and the call returns at once; buffers must stay alive until the stream
+ *     has passed the call.  Calls with no work (n_tokens == 0) return WPA_OK
+ *     and enqueue nothing.
+ *   - Arguments are validated on the host before anything is enqueued.  On a
+ *     nonzero status nothing has been enqueued and no output has been written.
+ *     WPA_ERR_LAUNCH reports a failed kernel launch (hipGetLastError).
+ *   - Layouts are C-contiguous ("[a][b][c]" = c fastest).
+ */
+#ifndef WPA_H
+#define WPA_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define WPA_HEAD_DIM 256
+#define WPA_PAGE_TOKENS 16
+/* Largest number of keys one query row may attend: the int32 PV accumulators
+ * (|code| <= 128, |v| <= 127 per key) cannot overflow below this. */
+#define WPA_MAX_KEYS_PER_ROW 131072
+
+typedef enum {
+  WPA_OK = 0,
+  WPA_ERR_NULL = 1,         /* a required pointer is NULL (with n_tokens > 0)          */
+  WPA_ERR_SHAPE = 2,        /* a size, count or scale is out of range                  */
+  WPA_ERR_UNSUPPORTED = 3,  /* bad dtype, misaligned pointer, or a limit exceeded      */
+  WPA_ERR_LAUNCH = 4        /* the HIP kernel launch failed                            */
+} wpa_status;
+
+typedef enum { WPA_F32 = 0, WPA_BF16 = 1 } wpa_dtype;
+
+/*
+ * Per-row quantization of Q (the method's first step: "one scale per query
+ * row", int8 tensor-core prefill attention page, "Why the attention, and why
+ * tensor cores").  A row is one (token, head) pair over the 256 channels:
+ *     amax = max |q|;   code = clamp(rint(q * (127 / amax)), -127, 127);
+ *     scale = amax / 127;           amax == 0 gives scale 0 and all-zero codes.
+ * Computed in float32 with IEEE division and round-half-to-even, so the codes
+ * are exactly those of that formula.
+ *
+ *   q        [n_tokens][n_q_heads][256], q_dtype WPA_BF16 or WPA_F32 (values
+ *            that are not finite give unspecified codes); 16-byte aligned.
+ *   q_i8     out [n_tokens][n_q_heads][256] int8; 16-byte aligned.
+ *   q_scale  out [n_tokens][n_q_heads] float32.
+ * Errors: NULL pointer -> WPA_ERR_NULL; n_tokens < 0 or n_q_heads <= 0 ->
+ * WPA_ERR_SHAPE; other dtype or misalignment -> WPA_ERR_UNSUPPORTED.
+ */
+wpa_status wpa_quantize_q_rows(const void* q, wpa_dtype q_dtype, int n_tokens, int n_q_heads,
+                               int8_t* q_i8, float* q_scale, hipStream_t stream);
+
+/*
+ * Prefill attention over the paged int8 KV pool (int8 tensor-core prefill
+ * attention page, "Why the attention, and why tensor cores"; window-off rule
+ * from its "Relation to open PRs"; StreamingLLM window from the fp16
+ * shared-memory tiles page, "Summary").
+ *
+ * Query row t (token t, prefill from position 0) of query head h attends
+ *     A(t) = { j <= t : window_blocks <= 0  or  j/16 < sink_blocks
+ *                                           or  j/16 >= rsb(t) },
+ *     rsb(t) = max(0, (t + 16)/16 - window_blocks),
+ * i.e. the first sink_blocks key blocks plus the last window_blocks blocks up
+ * to and including its own, causally; window_blocks <= 0 is full causal
+ * attention.  KV head of query head h is h / (n_q_heads / n_kv_heads).
+ *     s_j   = (q_i8 . k_i8[j]) * q_scale * k_scale[j] * softmax_scale
+ *     P_j   = exp(s_j - max s),  l = sum_{A(t)} P_j
+ *     P'_j  = P_j * v_scale[j]; per 16-key block: step ps = max P' / 127,
+ *             code_j = rint(P'_j / ps)            (int8, 0..127)
+ *     out   = sum_blocks ps * (code . v_i8) / l
+ * QK^T and PV run as int8 x int8 -> int32 matrix-core products.  The output
+ * matches that formula up to float32 rounding (see the design notes for the
+ * error budget); which codes a float32 tie flips is not specified.
+ *
+ *   q_i8, q_scale  from wpa_quantize_q_rows ([n_tokens][n_q_heads][256] int8,
+ *                  [n_tokens][n_q_heads] float32); q_i8 16-byte aligned.
+ *   k_pool, v_pool [n_pool_pages][16][n_kv_heads][256] int8, 16-byte aligned.
+ *   k_scale, v_scale [n_pool_pages][16][n_kv_heads] float32 (per token per KV
+ *                  head).  Scales of attended keys must be finite and > 0.
+ *   page_table     [ceil(n_tokens/16)] int32, logical block -> physical page.
+ *                  Entries must lie in [0, n_pool_pages); this is a caller
+ *                  precondition and is not checked on the device.
+ *   out            [n_tokens][n_q_heads][256], out_dtype WPA_BF16 (rounded to
+ *                  nearest even) or WPA_F32.
+ * Errors: NULL pointer -> WPA_ERR_NULL; n_tokens < 0, heads <= 0,
+ * n_q_heads % n_kv_heads != 0, n_pool_pages < ceil(n_tokens/16),
+ * sink_blocks < 0, softmax_scale not finite or <= 0 -> WPA_ERR_SHAPE;
+ * other dtype, misalignment, or more than WPA_MAX_KEYS_PER_ROW attended keys
+ * per row -> WPA_ERR_UNSUPPORTED.
+ */
+wpa_status wpa_prefill_attn_i8(const int8_t* q_i8, const float* q_scale,
+                               const int8_t* k_pool, const int8_t* v_pool,
+                               const float* k_scale, const float* v_scale,
+                               const int32_t* page_table, int n_pool_pages,
+                               int n_tokens, int n_q_heads, int n_kv_heads,
+                               int window_blocks, int sink_blocks, float softmax_scale,
+                               void* out, wpa_dtype out_dtype, hipStream_t stream);
+
+/*
+ * counts[t] = |A(t)| for t in [0, n_tokens), computed by walking the same key
+ * block list the attention kernel walks (the mask of the int8 tensor-core
+ * prefill attention page, "Why the attention, and why tensor cores": window
+ * start fixed per 16-row query tile, only the causal bound per row).
+ *   counts  out [n_tokens] int32.
+ * Errors: NULL -> WPA_ERR_NULL; n_tokens < 0 or sink_blocks < 0 -> WPA_ERR_SHAPE.
+ */
+wpa_status wpa_mask_counts(int n_tokens, int window_blocks, int sink_blocks, int32_t* counts,
+                           hipStream_t stream);
+
+/* Static, human-readable name of a status ("WPA_OK", ...; "unknown status"). */
+const char* wpa_status_string(wpa_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WPA_H */

@@ -188,24 +188,38 @@ def attention_exact(case, tiles=None) -> np.ndarray:
 # Mode (b): mirror of the int8 scheme
 # ----------------------------------------------------------------------------
 
-def _quantize_p_block(pv: np.ndarray):
+# A code is "near a tie" when its float32 argument x = P' * 127/mx lies within
+# TIE_WINDOW * x of k + 1/2.  At float32 precision either rounding of such a
+# code is a faithful result of the method: the arguments of an independent
+# float32 computation differ from these by about 1e-6 * x (8e-6 * x with
+# |s| ~ 50), so the window is several times that.
+TIE_WINDOW = 2.0 ** -14
+
+
+def _quantize_p_block(pv: np.ndarray, with_ties: bool = False):
     """Per-row int8 code of one 16-key block of P' = P * v_scale (>= 0).
 
     Decision in float32: mx = max P'; code = clip(rint(P' * (127/mx)), +-127);
     step ps = mx / 127.  Rows with no attended key (mx == 0) get code 0.
+    With with_ties, also returns the boolean mask of near-tie codes.
     """
     p32 = pv.astype(np.float32)
     mx = p32.max(axis=1)
     nz = mx > 0
     inv = (np.float32(127.0) / np.where(nz, mx, np.float32(1.0))).astype(np.float32)
-    codes = np.clip(np.rint((p32 * inv[:, None]).astype(np.float32)), -127, 127)
+    x = (p32 * inv[:, None]).astype(np.float32)
+    codes = np.clip(np.rint(x), -127, 127)
     codes[~nz] = 0.0
     ps = np.where(nz, mx.astype(np.float64) / 127.0, 0.0)
-    return codes.astype(np.float64), ps
+    if not with_ties:
+        return codes.astype(np.float64), ps
+    xd = x.astype(np.float64)
+    ties = (np.abs(xd - (np.floor(xd) + 0.5)) <= TIE_WINDOW * xd) & nz[:, None]
+    return codes.astype(np.float64), ps, ties
 
 
 def attention_int8_mirror(case, tiles=None, quantize_p: bool = True,
-                          q_codes=None, q_scale=None) -> np.ndarray:
+                          q_codes=None, q_scale=None, tie_slack: bool = False):
     """Mirror of the int8 path, fp64 except the quantization decisions.
 
       1. Q rows quantized (quantize_q_rows).
@@ -216,10 +230,14 @@ def attention_int8_mirror(case, tiles=None, quantize_p: bool = True,
          step ps = blockmax/127 (quantize_p=False keeps P' unquantized).
       6. O = sum over blocks of ps * (codes . v_i8), divided by l.
     Returns fp64 [n_tokens][n_q_heads][256]; unlisted tiles stay NaN.
+    With tie_slack, also returns slack[t,h,d] = sum over near-tie codes j of
+    ps_j * |v_i8[j,d]| / l: the most that re-rounding those codes the other
+    way can move the output.
     """
     N, Hq, Hkv = case.n_tokens, case.n_q_heads, case.n_kv_heads
     G = Hq // Hkv
     alpha = float(case.softmax_scale)
+    slack = np.full((N, Hq, HEAD_DIM), np.nan) if tie_slack else None
     if q_codes is None:
         q_codes, q_scale = quantize_q_rows(case.q_f32)
     out = np.full((N, Hq, HEAD_DIM), np.nan)
@@ -245,12 +263,19 @@ def attention_int8_mirror(case, tiles=None, quantize_p: bool = True,
                 l = p.sum(axis=1)
                 pv = np.where(mask, p * vs[None, :], 0.0)
                 o = np.zeros((len(rows), HEAD_DIM))
+                sl = np.zeros((len(rows), HEAD_DIM))
                 for b in blocks:
                     cols = kblk == b
-                    if quantize_p:
+                    if quantize_p and tie_slack:
+                        codes, ps, ties = _quantize_p_block(pv[:, cols], with_ties=True)
+                        o += ps[:, None] * (codes @ vi[cols])
+                        sl += ps[:, None] * (ties.astype(np.float64) @ np.abs(vi[cols]))
+                    elif quantize_p:
                         codes, ps = _quantize_p_block(pv[:, cols])
                         o += ps[:, None] * (codes @ vi[cols])
                     else:
                         o += pv[:, cols] @ vi[cols]
                 out[rows, h] = o / l[:, None]
-    return out
+                if tie_slack:
+                    slack[rows, h] = sl / l[:, None]
+    return (out, slack) if tie_slack else out

@@ -1,0 +1,138 @@
+"""C-ABI library checks that need no GPU: the built library loads, exports every
+function include/wpa.h declares, and rejects invalid arguments on the host
+(before any HIP call) with the documented status codes."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "wpa.h")
+LIB = os.path.join(ROOT, "windowed_int8_paged_amd", "libwpa.so")
+
+OK, NULL, SHAPE, UNSUP, LAUNCH = 0, 1, 2, 3, 4
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(wpa_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libwpa.so is not built (run __graft_entry__.build())")
+    L = ctypes.CDLL(LIB)
+    vp, ci, cf = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    L.wpa_prefill_attn_i8.argtypes = [vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, vp, ci, vp]
+    L.wpa_quantize_q_rows.argtypes = [vp, ci, ci, ci, vp, vp, vp]
+    L.wpa_mask_counts.argtypes = [ci, ci, ci, vp, vp]
+    L.wpa_status_string.argtypes = [ci]
+    L.wpa_status_string.restype = ctypes.c_char_p
+    return L
+
+
+def test_header_declares_the_three_entry_points():
+    fns = declared_functions()
+    for f in ("wpa_quantize_q_rows", "wpa_prefill_attn_i8", "wpa_mask_counts", "wpa_status_string"):
+        assert f in fns
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for f in declared_functions():
+        assert hasattr(lib, f), f
+
+
+def test_status_strings(lib):
+    assert lib.wpa_status_string(0) == b"WPA_OK"
+    for s in (1, 2, 3, 4):
+        assert lib.wpa_status_string(s).startswith(b"WPA_ERR")
+    assert lib.wpa_status_string(99) == b"unknown status"
+
+
+# Fake, never-dereferenced, 256-aligned addresses: every call below must be
+# rejected by host validation before the library touches the device.
+P = ctypes.c_void_p(0x100000)
+
+
+def attn(lib, **kw):
+    args = dict(q=P, qs=P, k=P, v=P, ks=P, vs=P, pt=P, n_pool=4, n=64, hq=4, hkv=2, W=0, S=0,
+                scale=0.0625, out=P, dtype=1)
+    args.update(kw)
+    return lib.wpa_prefill_attn_i8(args["q"], args["qs"], args["k"], args["v"], args["ks"], args["vs"],
+                                   args["pt"], args["n_pool"], args["n"], args["hq"], args["hkv"],
+                                   args["W"], args["S"], args["scale"], args["out"], args["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n=-1), SHAPE),
+    (dict(hq=0), SHAPE),
+    (dict(hkv=0), SHAPE),
+    (dict(hq=6, hkv=4), SHAPE),
+    (dict(S=-1), SHAPE),
+    (dict(scale=0.0), SHAPE),
+    (dict(scale=-1.0), SHAPE),
+    (dict(scale=float("inf")), SHAPE),
+    (dict(scale=float("nan")), SHAPE),
+    (dict(n_pool=3), SHAPE),              # 64 tokens need 4 pages
+    (dict(dtype=7), UNSUP),
+    (dict(q=None), NULL),
+    (dict(k=None), NULL),
+    (dict(pt=None), NULL),
+    (dict(out=None), NULL),
+    (dict(vs=None), NULL),
+    (dict(k=ctypes.c_void_p(0x100004)), UNSUP),   # pools must be 16-byte aligned
+    (dict(q=ctypes.c_void_p(0x100008)), UNSUP),
+    (dict(n=200000, n_pool=20000, W=0), UNSUP),  # more keys per row than int32 PV sums allow
+])
+def test_attention_rejects_invalid_arguments(lib, kw, status):
+    assert attn(lib, **kw) == status
+
+
+def test_attention_zero_tokens_is_a_noop(lib):
+    assert attn(lib, n=0, q=None, k=None, out=None, n_pool=0) == OK
+
+
+def test_quantize_rejects_invalid_arguments(lib):
+    q = lib.wpa_quantize_q_rows
+    assert q(P, 1, -1, 4, P, P, None) == SHAPE
+    assert q(P, 1, 4, 0, P, P, None) == SHAPE
+    assert q(P, 5, 4, 4, P, P, None) == UNSUP
+    assert q(None, 1, 4, 4, P, P, None) == NULL
+    assert q(P, 1, 4, 4, None, P, None) == NULL
+    assert q(P, 1, 4, 4, P, None, None) == NULL
+    assert q(ctypes.c_void_p(0x100002), 1, 4, 4, P, P, None) == UNSUP
+    assert q(None, 1, 0, 4, None, None, None) == OK
+
+
+def test_mask_counts_rejects_invalid_arguments(lib):
+    m = lib.wpa_mask_counts
+    assert m(-1, 0, 0, P, None) == SHAPE
+    assert m(10, 4, -1, P, None) == SHAPE
+    assert m(10, 4, 1, None, None) == NULL
+    assert m(0, 4, 1, None, None) == OK
+
+
+def test_host_block_list_matches_oracle_counts():
+    """The traversal the kernels use (csrc/wpa_common.h, tile_blocks) restated
+    by reading its integer formulas from the header and evaluating them for
+    every tile: it must give exactly the oracle's attended counts."""
+    import numpy as np
+    import oracle
+    src = open(os.path.join(ROOT, "windowed_int8_paged_amd", "csrc", "wpa_common.h")).read()
+    assert "tb.n_total = tb.n_sink + (n_blk_q - tb.win_start);" in src
+
+    def tile_blocks(qt, W, S):
+        n_blk_q = qt + 1
+        if W <= 0:
+            n_sink, win_start = 0, 0
+        else:
+            rsb = max(0, n_blk_q - W)
+            win_start, n_sink = rsb, min(S, rsb)
+        return n_sink + (n_blk_q - win_start)
+
+    for (n, W, S) in [(1000, 8, 1), (333, 3, 5), (4096, 256, 1), (500, 0, 3), (257, 1, 0)]:
+        counts = np.array([16 * (tile_blocks(t // 16, W, S) - 1) + t % 16 + 1 for t in range(n)])
+        assert np.array_equal(counts, oracle.mask_counts(n, W, S))

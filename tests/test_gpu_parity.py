@@ -1,0 +1,165 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Integer work is bit-exact (Q codes and scales, attended counts); the attention
+output is within max|d| <= 2e-3*max|O| of the int8 mirror and within 3e-2
+relative Frobenius of exact attention.  bf16 outputs are additionally allowed
+half a bf16 ulp, and must equal the round-to-nearest-even of the same kernel's
+fp32 output bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_util import check_parity, run, upload
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import windowed_int8_paged_amd  # noqa: F401  (fails loudly if the library is missing)
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+# ---------------------------------------------------------------- Q codes
+
+@pytest.mark.parametrize("container", ["bf16", "f32"])
+def test_quantize_q_rows_bit_exact(container):
+    import windowed_int8_paged_amd as wpa
+    rng = np.random.default_rng(77)
+    case = workloads.make_case(n_tokens=333, n_q_heads=6, n_kv_heads=2, window_blocks=0,
+                               sink_blocks=0, seed=5, q_outlier_frac=0.05)
+    q = case.q_f32.copy()
+    q[3, 1] = 0.0                                        # zero row
+    q[4, 2] = (np.arange(256) % 9 - 4).astype(np.float32) / 8 * (127 / 4)  # exact halves
+    q[5, 0, :7] = np.array([2.5, 3.5, -2.5, -3.5, 0.5, 1.5, 127.0], dtype=np.float32) / 8
+    q[5, 0, 7:] = 0
+    bits = workloads._round_to_bf16_bits(q)
+    qf = workloads._bf16_bits_to_f32(bits)
+    codes, scale = oracle.quantize_q_rows(qf)
+    if container == "bf16":
+        dq = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+    else:
+        dq = torch.from_numpy(qf).cuda()
+    q_i8, q_scale = wpa.quantize_q_rows(dq)
+    torch.cuda.synchronize()
+    assert np.array_equal(q_i8.cpu().numpy(), codes)
+    assert np.array_equal(q_scale.cpu().numpy().view(np.uint32), scale.view(np.uint32))
+    del rng
+
+
+# ---------------------------------------------------------------- mask counts
+
+@pytest.mark.parametrize("n,W,S", [(64, 0, 0), (1000, 8, 1), (4096, 256, 1), (777, 3, 5),
+                                   (17, 1, 0), (5000, 2, 0), (16384, 0, 0), (333, -4, 2)])
+def test_mask_counts_bit_exact(n, W, S):
+    import windowed_int8_paged_amd as wpa
+    got = wpa.mask_counts(n, W, S).cpu().numpy()
+    assert np.array_equal(got, oracle.mask_counts(n, W, S))
+
+
+@pytest.mark.parametrize("name,total", [("32k", 126074880), ("64k", 260571136)])
+def test_mask_counts_full_size(name, total):
+    import windowed_int8_paged_amd as wpa
+    cfg = workloads.CONFIGS[name]
+    n, W, S = cfg["n_tokens"], cfg["window_blocks"], cfg["sink_blocks"]
+    got = wpa.mask_counts(n, W, S).cpu().numpy()
+    assert int(got.astype(np.int64).sum()) == total
+    assert got.max() == 4112
+    for tile in (0, 1, 255, 256, 257, n // 32, n // 16 - 1):
+        rows = oracle.tile_rows(n, tile)
+        keys = np.arange(0, rows[-1] + 1)
+        assert np.array_equal(got[rows], oracle.attended_mask(rows, keys, W, S).sum(axis=1))
+
+
+# ---------------------------------------------------------------- small cases, all rows
+
+SMALL = [
+    # n, hq, hkv, W, S, seed
+    (64, 2, 1, 0, 0, 1),        # tiny-like, full causal
+    (100, 4, 4, 2, 1, 2),       # MHA, ragged tail
+    (1000, 8, 2, 8, 1, 3),      # GQA-4, windowed, ragged
+    (777, 6, 2, 3, 0, 4),       # GQA-3 (odd: a padded head), no sink
+    (515, 16, 2, 4, 2, 5),      # GQA-8 (4 waves per workgroup)
+    (300, 2, 2, 1, 0, 6),       # window of one block
+    (90, 4, 1, 1, 5, 7),        # sink larger than the window start
+    (33, 4, 2, 300, 1, 8),      # window wider than the sequence
+    (1, 4, 2, 0, 0, 9),         # a single token
+    (16, 8, 2, 1, 1, 10),       # exactly one tile
+]
+
+
+@pytest.mark.parametrize("n,hq,hkv,W,S,seed", SMALL)
+def test_small_parity(n, hq, hkv, W, S, seed):
+    case = workloads.make_case(n_tokens=n, n_q_heads=hq, n_kv_heads=hkv, window_blocks=W,
+                               sink_blocks=S, seed=seed, extra_pool_frac=0.3)
+    dev = upload(case)
+    _say(f"small case n={n} hq={hq} hkv={hkv} W={W} S={S}")
+    _, _, o32 = run(case, dev, out_dtype=torch.float32)
+    check_parity(case, o32, label="f32")
+    _, _, o16 = run(case, dev, out_dtype=torch.bfloat16)
+    check_parity(case, o16, label="bf16")
+    assert torch.equal(o16, o32.to(torch.bfloat16))
+
+
+def test_outlier_rows_small():
+    """Outlier Q rows and saturated K tokens with log-uniform scales, full causal."""
+    case = workloads.make_case(n_tokens=1500, n_q_heads=8, n_kv_heads=2, window_blocks=0,
+                               sink_blocks=0, seed=11, scale_lo=1e-3, scale_hi=5e-2,
+                               log_uniform_scales=True, q_outlier_frac=0.01, k_saturated_frac=0.02)
+    _, _, o32 = run(case, out_dtype=torch.float32)
+    check_parity(case, o32, label="outliers f32")
+
+
+def test_tiny_config_both_containers():
+    case = workloads.make_config("tiny")
+    dev = upload(case)
+    _, _, a = run(case, dev, q_key="q_bf16", out_dtype=torch.float32)
+    _, _, b = run(case, dev, q_key="q_f32", out_dtype=torch.float32)
+    assert torch.equal(a, b)
+    r = check_parity(case, a, label="tiny")
+    _say(f"tiny parity {r}")
+
+
+def test_deterministic_and_stray_page_safe():
+    """Run twice bitwise equal; unused pool pages carry NaN scales and random
+    codes, so any read of them would make the output non-finite."""
+    case = workloads.make_case(n_tokens=700, n_q_heads=8, n_kv_heads=2, window_blocks=4,
+                               sink_blocks=1, seed=12, extra_pool_frac=1.0)
+    dev = upload(case)
+    _, _, a = run(case, dev)
+    _, _, b = run(case, dev)
+    assert torch.equal(a, b)
+    assert torch.isfinite(a.float()).all()
+
+
+# ---------------------------------------------------------------- the five workloads, sampled
+
+def sample_tiles(n_tokens, window_blocks):
+    nt = (n_tokens + 15) // 16
+    tiles = {0, 1, 2, nt // 3, nt // 2, nt - 2, nt - 1}
+    if window_blocks > 0:
+        tiles |= {window_blocks - 1, window_blocks, window_blocks + 1}
+    return sorted(t for t in tiles if 0 <= t < nt)
+
+
+@pytest.mark.parametrize("name", ["4k", "32k", "64k", "16k_full"])
+def test_config_sampled_parity(name):
+    case = workloads.make_config(name)
+    dev = upload(case)
+    tiles = sample_tiles(case.n_tokens, case.window_blocks)
+    _say(f"config {name}: tiles {tiles}")
+    _, _, o16 = run(case, dev, out_dtype=torch.bfloat16)        # the benchmarked launch
+    r16 = check_parity(case, o16, tiles=tiles, label=f"{name} bf16")
+    _, _, o32 = run(case, dev, out_dtype=torch.float32)
+    r32 = check_parity(case, o32, tiles=tiles, label=f"{name} f32")
+    assert torch.equal(o16, o32.to(torch.bfloat16))
+    assert torch.isfinite(o16.float()).all()
+    _say(f"config {name}: bf16 {r16} f32 {r32}")

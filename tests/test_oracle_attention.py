@@ -272,3 +272,37 @@ def test_p_block_codes():
     # multiplier 31.75: 1.0 -> 31.75 -> 32
     assert codes[2].tolist() == [127, 32, 0, 127]
     np.testing.assert_allclose(ps[[0, 2]], [0.5 / 127, 4.0 / 127])
+
+
+def test_mirror_tie_slack_covers_an_exact_tie():
+    """Equal scores and v_scale(key0) = 2 v_scale(key1) put key 1's code
+    argument at exactly 63.5: rint gives 64 (half-even), 63 is equally
+    faithful, and the reported slack is exactly the effect of that choice."""
+    case = workloads.make_case(n_tokens=2, n_q_heads=1, n_kv_heads=1, window_blocks=0,
+                               sink_blocks=0, seed=1, poison_unused=False)
+    case.q_f32[:] = 0
+    case.k_pool[:] = 0
+    p0 = case.page_table[0]
+    case.v_scale[p0, 0, 0] = 2.0 ** -6
+    case.v_scale[p0, 1, 0] = 2.0 ** -7
+    out, slack = oracle.attention_int8_mirror(case, tie_slack=True)
+    v1 = np.abs(case.v_pool[p0, 1, 0].astype(np.float64))
+    ps = 2.0 ** -6 / 127
+    np.testing.assert_allclose(slack[1, 0], ps * v1 / 2.0, rtol=1e-12)
+    assert np.all(slack[0, 0] == 0)
+    v0 = case.v_pool[p0, 0, 0].astype(np.float64)
+    vv1 = case.v_pool[p0, 1, 0].astype(np.float64)
+    np.testing.assert_allclose(out[1, 0], ps * (127 * v0 + 64 * vv1) / 2.0, rtol=1e-12)
+    # output without the slack request is the same array
+    np.testing.assert_array_equal(oracle.attention_int8_mirror(case), out)
+
+
+def test_mirror_tie_slack_is_small_on_random_inputs():
+    """Near-tie codes are a small share, so the slack stays far below the
+    2e-3 * max|O| bar except in short rows where one code weighs a lot."""
+    case = small_case(n=300, hq=4, hkv=2, W=4, S=1, seed=33)
+    out, slack = oracle.attention_int8_mirror(case, tie_slack=True)
+    mo = np.abs(out).max()
+    assert np.mean(slack) < 1e-4 * mo
+    assert np.median(slack) == 0.0
+    assert np.mean(slack[200:] > 0) < 0.4

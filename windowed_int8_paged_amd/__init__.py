@@ -1,0 +1,133 @@
+"""Python binding of libwpa.so: windowed int8 paged prefill attention on MI355X.
+
+Argument marshalling only.  Every step of the path runs in the library's HIP
+kernels; PyTorch provides device memory and the current stream.  There is no
+CPU fallback: if the built library is missing, importing this package raises.
+
+Entry points mirror the C ABI in include/wpa.h:
+    quantize_q_rows(q, q_i8=None, q_scale=None)      -> (q_i8, q_scale)
+    prefill_attn_i8(q_i8, q_scale, k_pool, v_pool, k_scale, v_scale, page_table,
+                    window_blocks, sink_blocks, softmax_scale, out=None,
+                    out_dtype=torch.bfloat16)          -> out
+    mask_counts(n_tokens, window_blocks, sink_blocks, counts=None, device=None) -> counts
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["quantize_q_rows", "prefill_attn_i8", "mask_counts", "lib", "LIB_PATH",
+           "HEAD_DIM", "PAGE_TOKENS", "WpaError"]
+
+HEAD_DIM = 256
+PAGE_TOKENS = 16
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libwpa.so")
+
+WPA_F32, WPA_BF16 = 0, 1
+
+
+class WpaError(RuntimeError):
+    pass
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run windowed_int8_paged_amd.build.build()")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, ci, cf = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    L.wpa_quantize_q_rows.argtypes = [vp, ci, ci, ci, vp, vp, vp]
+    L.wpa_quantize_q_rows.restype = ci
+    L.wpa_prefill_attn_i8.argtypes = [vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, vp, ci, vp]
+    L.wpa_prefill_attn_i8.restype = ci
+    L.wpa_mask_counts.argtypes = [ci, ci, ci, vp, vp]
+    L.wpa_mask_counts.restype = ci
+    L.wpa_status_string.argtypes = [ci]
+    L.wpa_status_string.restype = ctypes.c_char_p
+    return L
+
+
+lib = _load()
+
+
+def _check(status: int):
+    if status != 0:
+        raise WpaError(lib.wpa_status_string(status).decode())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _dev(t, name, dtype, shape=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t
+
+
+def quantize_q_rows(q, q_i8=None, q_scale=None):
+    """q: [n_tokens][n_q_heads][256] bf16 or f32 on the device."""
+    if q.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("q must be bfloat16 or float32")
+    _dev(q, "q", q.dtype)
+    n, hq, d = q.shape
+    if d != HEAD_DIM:
+        raise ValueError("head_dim must be 256")
+    if q_i8 is None:
+        q_i8 = torch.empty((n, hq, d), dtype=torch.int8, device=q.device)
+    if q_scale is None:
+        q_scale = torch.empty((n, hq), dtype=torch.float32, device=q.device)
+    _dev(q_i8, "q_i8", torch.int8, (n, hq, d))
+    _dev(q_scale, "q_scale", torch.float32, (n, hq))
+    _check(lib.wpa_quantize_q_rows(_ptr(q), WPA_BF16 if q.dtype == torch.bfloat16 else WPA_F32,
+                                   n, hq, _ptr(q_i8), _ptr(q_scale), _stream(q.device)))
+    return q_i8, q_scale
+
+
+def prefill_attn_i8(q_i8, q_scale, k_pool, v_pool, k_scale, v_scale, page_table,
+                    window_blocks, sink_blocks, softmax_scale, out=None, out_dtype=torch.bfloat16):
+    """Paged int8 prefill attention; see include/wpa.h for the definition."""
+    _dev(q_i8, "q_i8", torch.int8)
+    n, hq, d = q_i8.shape
+    _dev(q_scale, "q_scale", torch.float32, (n, hq))
+    _dev(k_pool, "k_pool", torch.int8)
+    n_pool, page, hkv, d2 = k_pool.shape
+    if page != PAGE_TOKENS or d2 != HEAD_DIM or d != HEAD_DIM:
+        raise ValueError("pool pages must be [16][n_kv_heads][256]")
+    _dev(v_pool, "v_pool", torch.int8, k_pool.shape)
+    _dev(k_scale, "k_scale", torch.float32, (n_pool, page, hkv))
+    _dev(v_scale, "v_scale", torch.float32, (n_pool, page, hkv))
+    _dev(page_table, "page_table", torch.int32)
+    if page_table.numel() < (n + PAGE_TOKENS - 1) // PAGE_TOKENS:
+        raise ValueError("page_table is shorter than ceil(n_tokens/16)")
+    if out is None:
+        out = torch.empty((n, hq, d), dtype=out_dtype, device=q_i8.device)
+    if out.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("out must be bfloat16 or float32")
+    _dev(out, "out", out.dtype, (n, hq, d))
+    _check(lib.wpa_prefill_attn_i8(
+        _ptr(q_i8), _ptr(q_scale), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale),
+        _ptr(page_table), n_pool, n, hq, hkv, int(window_blocks), int(sink_blocks),
+        float(softmax_scale), _ptr(out), WPA_BF16 if out.dtype == torch.bfloat16 else WPA_F32,
+        _stream(q_i8.device)))
+    return out
+
+
+def mask_counts(n_tokens, window_blocks, sink_blocks, counts=None, device=None):
+    if counts is None:
+        counts = torch.empty((n_tokens,), dtype=torch.int32, device=device or "cuda")
+    _dev(counts, "counts", torch.int32, (n_tokens,))
+    _check(lib.wpa_mask_counts(int(n_tokens), int(window_blocks), int(sink_blocks), _ptr(counts),
+                               _stream(counts.device)))
+    return counts

@@ -1,0 +1,100 @@
+// C ABI of the library: host-side validation, then the kernel launchers.
+// Every check runs before anything is enqueued, so a nonzero status means no
+// work was queued and no output was touched.
+
+#include <cmath>
+#include <cstdint>
+
+#include "wpa.h"
+#include "wpa_launch.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+long ceil_div(long a, long b) { return (a + b - 1) / b; }
+
+// Largest number of keys any row attends: full causal -> n_tokens; otherwise
+// the last 'window_blocks' blocks plus the sink blocks, capped by n_tokens.
+long max_keys_per_row(int n_tokens, int window_blocks, int sink_blocks) {
+  if (window_blocks <= 0) return n_tokens;
+  const long w = (long)WPA_PAGE_TOKENS * ((long)window_blocks + (long)sink_blocks);
+  return w < n_tokens ? w : n_tokens;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* wpa_status_string(wpa_status s) {
+  switch (s) {
+    case WPA_OK: return "WPA_OK";
+    case WPA_ERR_NULL: return "WPA_ERR_NULL: a required pointer is NULL";
+    case WPA_ERR_SHAPE: return "WPA_ERR_SHAPE: a size, count or scale is out of range";
+    case WPA_ERR_UNSUPPORTED: return "WPA_ERR_UNSUPPORTED: dtype, alignment or a size limit";
+    case WPA_ERR_LAUNCH: return "WPA_ERR_LAUNCH: the HIP kernel launch failed";
+  }
+  return "unknown status";
+}
+
+wpa_status wpa_quantize_q_rows(const void* q, wpa_dtype q_dtype, int n_tokens, int n_q_heads, int8_t* q_i8,
+                               float* q_scale, hipStream_t stream) {
+  if (n_tokens < 0 || n_q_heads <= 0) return WPA_ERR_SHAPE;
+  if (q_dtype != WPA_BF16 && q_dtype != WPA_F32) return WPA_ERR_UNSUPPORTED;
+  if (n_tokens == 0) return WPA_OK;
+  if (!q || !q_i8 || !q_scale) return WPA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(q_i8)) return WPA_ERR_UNSUPPORTED;
+  if ((long)n_tokens * n_q_heads * 32 > 0x7fffffffL * 256L) return WPA_ERR_UNSUPPORTED;
+  if (wpa::launch_quantize_q_rows(q, q_dtype == WPA_BF16, n_tokens, n_q_heads, q_i8, q_scale, stream) !=
+      hipSuccess)
+    return WPA_ERR_LAUNCH;
+  return WPA_OK;
+}
+
+wpa_status wpa_prefill_attn_i8(const int8_t* q_i8, const float* q_scale, const int8_t* k_pool,
+                               const int8_t* v_pool, const float* k_scale, const float* v_scale,
+                               const int32_t* page_table, int n_pool_pages, int n_tokens, int n_q_heads,
+                               int n_kv_heads, int window_blocks, int sink_blocks, float softmax_scale,
+                               void* out, wpa_dtype out_dtype, hipStream_t stream) {
+  if (n_tokens < 0 || n_q_heads <= 0 || n_kv_heads <= 0 || n_q_heads % n_kv_heads != 0) return WPA_ERR_SHAPE;
+  if (sink_blocks < 0 || !std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return WPA_ERR_SHAPE;
+  if (n_pool_pages < ceil_div(n_tokens, WPA_PAGE_TOKENS) || n_pool_pages < 0) return WPA_ERR_SHAPE;
+  if (out_dtype != WPA_BF16 && out_dtype != WPA_F32) return WPA_ERR_UNSUPPORTED;
+  if (n_tokens == 0) return WPA_OK;
+  if (!q_i8 || !q_scale || !k_pool || !v_pool || !k_scale || !v_scale || !page_table || !out)
+    return WPA_ERR_NULL;
+  if (!aligned16(q_i8) || !aligned16(k_pool) || !aligned16(v_pool)) return WPA_ERR_UNSUPPORTED;
+  if (max_keys_per_row(n_tokens, window_blocks, sink_blocks) > WPA_MAX_KEYS_PER_ROW) return WPA_ERR_UNSUPPORTED;
+  const long n_tiles = ceil_div(n_tokens, WPA_PAGE_TOKENS);
+  if (n_tiles * n_kv_heads * ((n_q_heads / n_kv_heads + 1) / 2) > 0x7fffffffL) return WPA_ERR_UNSUPPORTED;
+
+  wpa::AttnArgs a = {};
+  a.q_i8 = q_i8;
+  a.q_scale = q_scale;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.page_table = page_table;
+  a.out = out;
+  a.n_tokens = n_tokens;
+  a.n_q_heads = n_q_heads;
+  a.n_kv_heads = n_kv_heads;
+  a.window_blocks = window_blocks;
+  a.sink_blocks = sink_blocks;
+  a.softmax_scale = softmax_scale;
+  if (wpa::launch_prefill_attn(a, out_dtype == WPA_BF16, stream) != hipSuccess) return WPA_ERR_LAUNCH;
+  return WPA_OK;
+}
+
+wpa_status wpa_mask_counts(int n_tokens, int window_blocks, int sink_blocks, int32_t* counts,
+                           hipStream_t stream) {
+  if (n_tokens < 0 || sink_blocks < 0) return WPA_ERR_SHAPE;
+  if (n_tokens == 0) return WPA_OK;
+  if (!counts) return WPA_ERR_NULL;
+  if (wpa::launch_mask_counts(n_tokens, window_blocks, sink_blocks, counts, stream) != hipSuccess)
+    return WPA_ERR_LAUNCH;
+  return WPA_OK;
+}
+
+}  // extern "C"

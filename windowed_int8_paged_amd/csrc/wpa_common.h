@@ -1,0 +1,43 @@
+// Device-side pieces shared by the attention and mask-count kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace wpa {
+
+constexpr int kHeadDim = 256;
+constexpr int kPage = 16;
+
+// Key blocks visited by one 16-row query tile.  The query tile is aligned to
+// the 16-token page, so the window start is one value for the whole tile and
+// only the causal bound differs between its rows (int8 tensor-core prefill
+// attention page, "Why the attention, and why tensor cores").  The list is
+// the sink blocks [0, n_sink) followed by the window blocks
+// [win_start, qt]; window_blocks <= 0 means every block up to the diagonal
+// ("Relation to open PRs").  The diagonal block qt is always the last entry
+// and is the only one that needs a per-row (causal) mask.
+struct TileBlocks {
+  int n_sink;     // leading sink blocks 0 .. n_sink-1
+  int win_start;  // first window block
+  int n_total;    // list length = n_sink + (qt - win_start + 1)
+
+  __host__ __device__ int block(int i) const { return i < n_sink ? i : win_start + (i - n_sink); }
+};
+
+__host__ __device__ inline TileBlocks tile_blocks(int qt, int window_blocks, int sink_blocks) {
+  TileBlocks tb;
+  const int n_blk_q = qt + 1;  // (t + 16) / 16 for every row t of the tile
+  if (window_blocks <= 0) {
+    tb.n_sink = 0;
+    tb.win_start = 0;
+  } else {
+    const int rsb = n_blk_q - window_blocks > 0 ? n_blk_q - window_blocks : 0;
+    tb.win_start = rsb;
+    tb.n_sink = sink_blocks < rsb ? sink_blocks : rsb;  // sink blocks left of the window
+  }
+  tb.n_total = tb.n_sink + (n_blk_q - tb.win_start);
+  return tb;
+}
+
+}  // namespace wpa

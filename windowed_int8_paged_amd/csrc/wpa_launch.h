@@ -1,0 +1,32 @@
+// Kernel launchers behind the C ABI (host side, arguments already validated).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace wpa {
+
+struct AttnArgs {
+  const int8_t* q_i8;
+  const float* q_scale;
+  const int8_t* k_pool;
+  const int8_t* v_pool;
+  const float* k_scale;
+  const float* v_scale;
+  const int32_t* page_table;
+  void* out;
+  int n_tokens, n_q_heads, n_kv_heads;
+  int window_blocks, sink_blocks;
+  float softmax_scale;
+  // filled in by the launcher
+  int G, n_pairs, hgroups, n_tiles;
+  float row_mul;
+};
+
+hipError_t launch_quantize_q_rows(const void* q, bool bf16, int n_tokens, int n_q_heads, int8_t* q_i8,
+                                  float* q_scale, hipStream_t stream);
+hipError_t launch_mask_counts(int n_tokens, int window_blocks, int sink_blocks, int32_t* counts,
+                              hipStream_t stream);
+hipError_t launch_prefill_attn(const AttnArgs& args, bool out_bf16, hipStream_t stream);
+
+}  // namespace wpa

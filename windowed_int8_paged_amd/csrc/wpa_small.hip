@@ -1,0 +1,92 @@
+// Q row quantization and mask counts: the two small kernels of the path.
+//
+// Q quantization follows the int8 tensor-core prefill attention page, section
+// "Why the attention, and why tensor cores" (one scale per query row).  It is
+// a pure HBM stream: each row is 256 values, read once, written once as int8
+// plus one float scale.  One wave handles two rows, 32 lanes per row, 8
+// values per lane, so every lane issues one 16-byte load (bf16) and one
+// 8-byte store.
+
+#include "wpa_common.h"
+#include "wpa_launch.h"
+
+namespace wpa {
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void quantize_q_rows_kernel(const void* __restrict__ q,
+                                                              int8_t* __restrict__ q_i8,
+                                                              float* __restrict__ q_scale,
+                                                              long n_rows) {
+  const long row = ((long)blockIdx.x * blockDim.x + threadIdx.x) >> 5;
+  const int sub = threadIdx.x & 31;  // 8 channels each
+  if (row >= n_rows) return;         // whole half-waves drop out together
+
+  float v[8];
+  if (BF16) {
+    const uint4 raw = reinterpret_cast<const uint4*>(q)[row * 32 + sub];
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(q) + row * 64 + sub * 2;
+    const float4 a = p[0], b = p[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+#pragma unroll
+  for (int off = 16; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 32));
+
+  // IEEE division and round-half-to-even, as the definition states.
+  const float inv = amax > 0.f ? 127.0f / amax : 0.f;
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float c = rintf(v[i] * inv);
+    c = fminf(fmaxf(c, -127.f), 127.f);
+    const uint32_t b = (uint32_t)(int32_t)c & 0xffu;
+    if (i < 4) lo |= b << (8 * i);
+    else hi |= b << (8 * (i - 4));
+  }
+  reinterpret_cast<uint2*>(q_i8)[row * 32 + sub] = make_uint2(lo, hi);
+  if (sub == 0) q_scale[row] = amax > 0.f ? amax / 127.0f : 0.f;
+}
+
+// counts[t] = number of keys row t attends: every listed block but the
+// diagonal one is attended whole, the diagonal contributes t%16 + 1 keys.
+__global__ __launch_bounds__(256) void mask_counts_kernel(int n_tokens, int window_blocks,
+                                                          int sink_blocks, int32_t* __restrict__ counts) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= n_tokens) return;
+  const int qt = t / kPage;
+  const TileBlocks tb = tile_blocks(qt, window_blocks, sink_blocks);
+  counts[t] = kPage * (tb.n_total - 1) + (t - kPage * qt + 1);
+}
+
+hipError_t launch_quantize_q_rows(const void* q, bool bf16, int n_tokens, int n_q_heads, int8_t* q_i8,
+                                  float* q_scale, hipStream_t stream) {
+  const long n_rows = (long)n_tokens * n_q_heads;
+  const long threads = n_rows * 32;
+  const unsigned blocks = (unsigned)((threads + 255) / 256);
+  if (bf16)
+    hipLaunchKernelGGL(quantize_q_rows_kernel<true>, dim3(blocks), dim3(256), 0, stream, q, q_i8, q_scale, n_rows);
+  else
+    hipLaunchKernelGGL(quantize_q_rows_kernel<false>, dim3(blocks), dim3(256), 0, stream, q, q_i8, q_scale, n_rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_mask_counts(int n_tokens, int window_blocks, int sink_blocks, int32_t* counts,
+                              hipStream_t stream) {
+  const unsigned blocks = (unsigned)((n_tokens + 255) / 256);
+  hipLaunchKernelGGL(mask_counts_kernel, dim3(blocks), dim3(256), 0, stream, n_tokens, window_blocks,
+                     sink_blocks, counts);
+  return hipGetLastError();
+}
+
+}  // namespace wpa
