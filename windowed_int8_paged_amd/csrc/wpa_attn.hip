@@ -30,17 +30,18 @@
 #include "wpa_launch.h"
 
 #ifndef WPA_NPL
-#define WPA_NPL 3
+#define WPA_NPL 2
 #endif
 
 namespace wpa {
 
+typedef int v2i __attribute__((ext_vector_type(2)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+#define WPA_LDS __attribute__((address_space(3)))
 
-constexpr int kItKeys = 32;    // keys per loop iteration (two pages)
-constexpr int kKStride = 272;  // LDS bytes per staged key row: 256 + 16 pad
-constexpr int kVStride = 48;   // LDS bytes per channel row of staged V^T: 32 + 16 pad
+constexpr int kItKeys = 32;                 // keys per loop iteration (two pages)
+constexpr int kStage = kItKeys * kHeadDim;  // bytes of one staged K or V tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kMagic = 8388608.0f;  // 2^23: x + 2^23 has x in its low 23 bits
 
@@ -55,12 +56,15 @@ struct FixedPoint<2> {
   static constexpr float kXmax = 32512.f;  // top digit (x + 128) >> 8 stays <= 127
 };
 
-struct alignas(16) Smem {
-  int8_t k[kItKeys * kKStride];
-  int8_t vt[kHeadDim * kVStride];
-  float ks[kItKeys];   // k_scale
-  float lvs[kItKeys];  // log2(v_scale)
-  float rvs[kItKeys];  // 1 / v_scale
+// One stage buffer.  K and V tiles are row-major (row = key of the
+// iteration, 256 bytes) with the 16-byte chunk c of row r stored in slot
+// c ^ (r & 15), so the operand reads below hit all 64 banks once.  The two
+// buffers are separate LDS objects so the compiler can tell that reads of one
+// never alias the asynchronous copies into the other.
+struct alignas(16) Stage {
+  int8_t k[kStage];
+  int8_t v[kStage];
+  float sc[2][kItKeys];  // [k_scale, v_scale][key]
 };
 
 __device__ inline float xhalf_max(float x) {
@@ -72,97 +76,84 @@ __device__ inline float xhalf_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-__device__ inline uint32_t byte_of(uint32_t w, int k) { return (w >> (8 * k)) & 0xffu; }
+// Physical pages of list entries 2it and 2it+1 (an empty second slot reuses
+// the first page: its keys are masked).
+struct PagePair {
+  long p0, p1;
+};
+__device__ inline PagePair page_pair(const int32_t* __restrict__ pt, const TileBlocks& tb, int it) {
+  const int li = 2 * it;
+  const int b0 = tb.block(li);
+  const int b1 = li + 1 < tb.n_total ? tb.block(li + 1) : b0;
+  PagePair pp;
+  pp.p0 = pt[b0];
+  pp.p1 = pt[b1];
+  return pp;
+}
 
-// Stage the two pages of iteration `it` (list entries 2it, 2it+1) into LDS.
-// Entries past the end of the list are staged as zero keys with zero scales;
-// their scores are masked.
-template <int NTHR, bool WITH_V>
-__device__ inline void stage(Smem& sm, const AttnArgs& a, const TileBlocks& tb, int it, int kvh) {
-  const int tid = threadIdx.x;
-  const long row_elems = (long)a.n_kv_heads * kHeadDim;  // pool row stride (bytes)
-  const int li0 = 2 * it;
-  const bool ok1 = li0 + 1 < tb.n_total;
-  const long phys0 = a.page_table[tb.block(li0)];
-  const long phys1 = ok1 ? (long)a.page_table[tb.block(li0 + 1)] : 0;
-  // K rows: 32 keys x 16 chunks of 16 bytes
+// Asynchronous global->LDS copy of 16 (or 4) bytes per lane: lane l's bytes
+// land at lds_base + 16*l (4*l).  Issued as inline assembly so the compiler
+// does not model the in-flight LDS write; the kernel orders it explicitly
+// with wait_stage() and a workgroup barrier before any read of that buffer.
+__device__ inline uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const WPA_LDS void*)p;
+}
+__device__ inline void dma16(const void* src, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_base) : "memory", "m0");
+}
+__device__ inline void dma4(const void* src, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(lds_base) : "memory", "m0");
+}
+
+// Issue the copies of one iteration's two pages: 8 K and 8 V row groups of 4
+// rows (1 KB, one 16-byte chunk per lane), shared out over the workgroup's
+// waves, plus the 32 K and 32 V scales.
+template <int WPG>
+__device__ inline void issue_stage(Stage& st, const AttnArgs& a, int kvh, PagePair pg, int wave, int lane) {
+  const long row_bytes = (long)a.n_kv_heads * kHeadDim;
+  const int s = lane & 15;
 #pragma unroll
-  for (int c0 = 0; c0 < kItKeys * 16; c0 += NTHR) {
-    const int c = c0 + tid;
-    const int key = c >> 4, ch = c & 15;
-    const bool second = key >= 16;
-    uint4 val = {0u, 0u, 0u, 0u};
-    if (!second || ok1) {
-      const long phys = second ? phys1 : phys0;
-      const int8_t* src = a.k_pool + (phys * kPage + (key & 15)) * row_elems + (long)kvh * kHeadDim + ch * 16;
-      val = *reinterpret_cast<const uint4*>(src);
-    }
-    *reinterpret_cast<uint4*>(sm.k + key * kKStride + ch * 16) = val;
+  for (int j = 0; j < 16 / WPG; ++j) {
+    const int g = wave + WPG * j;  // wave-uniform
+    const bool isv = g >= 8;
+    const int r0 = 4 * (g & 7);
+    const int r = r0 + (lane >> 4);
+    const long phys = r < 16 ? pg.p0 : pg.p1;
+    const int8_t* src = (isv ? a.v_pool : a.k_pool) + (phys * kPage + (r & 15)) * row_bytes +
+                        (long)kvh * kHeadDim + 16 * (s ^ (r & 15));
+    dma16(src, lds_addr((isv ? st.v : st.k) + r0 * kHeadDim));
   }
-  if (tid < kItKeys) {
-    const int key = tid;
-    const bool second = key >= 16;
-    float k_s = 0.f, lv = 0.f, rv = 0.f;
-    if (!second || ok1) {
-      const long phys = second ? phys1 : phys0;
-      const long idx = (phys * kPage + (key & 15)) * a.n_kv_heads + kvh;
-      const float v_s = a.v_scale[idx];
-      k_s = a.k_scale[idx];
-      lv = log2f(v_s);
-      rv = 1.0f / v_s;
-    }
-    sm.ks[key] = k_s;
-    sm.lvs[key] = lv;
-    sm.rvs[key] = rv;
-  }
-  if (!WITH_V) return;
-  // V^T: 8 groups of 4 tokens x 16 chunks of 16 channels.  Keys of a channel
-  // row are stored in the order the PV operand reads them: position
-  // 16h + 4i + k holds key 8i + 4h + k.
-#pragma unroll
-  for (int u0 = 0; u0 < 128; u0 += NTHR) {
-    const int u = u0 + tid;
-    if (NTHR > 128 && u >= 128) break;
-    const int tg = u >> 4, dc = u & 15;
-    const int key0 = 4 * tg;
-    const bool second = key0 >= 16;
-    uint4 r[4] = {};
-    if (!second || ok1) {
-      const long phys = second ? phys1 : phys0;
-      const int8_t* src = a.v_pool + (phys * kPage + (key0 & 15)) * row_elems + (long)kvh * kHeadDim + dc * 16;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) r[i] = *reinterpret_cast<const uint4*>(src + i * row_elems);
-    }
-    const int pos0 = 16 * (tg & 1) + 4 * (tg >> 1);
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const uint32_t a0 = (&r[0].x)[w], a1 = (&r[1].x)[w], a2 = (&r[2].x)[w], a3 = (&r[3].x)[w];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t b = byte_of(a0, k) | (byte_of(a1, k) << 8) | (byte_of(a2, k) << 16) | (byte_of(a3, k) << 24);
-        *reinterpret_cast<uint32_t*>(sm.vt + (dc * 16 + 4 * w + k) * kVStride + pos0) = b;
-      }
-    }
+  if (wave == 0) {
+    const int key = lane & 31;
+    const long phys = key < 16 ? pg.p0 : pg.p1;
+    const float* src = (lane < 32 ? a.k_scale : a.v_scale) + (phys * kPage + (key & 15)) * a.n_kv_heads + kvh;
+    dma4(src, lds_addr(&st.sc[0][0]));
   }
 }
 
-// S^T for the 32 staged keys x this wave's 32 query rows.
-__device__ inline v16i qk_tile(const Smem& sm, const v4i (&qf)[8], int lane) {
+__device__ inline void wait_stage() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// S^T for the 32 staged keys x this wave's 32 query rows: lane l owns query
+// row l%32 and keys 8(v/4) + 4(l/32) + v%4 of register v.  Both operands come
+// from LDS tiles with the chunk swizzle c ^ (row & 15).
+__device__ inline v16i qk_tile(const int8_t* kb, const int8_t* qb, int lane) {
   v16i s = {};
-  const int8_t* krow = sm.k + (lane & 31) * kKStride + 16 * (lane >> 5);
+  const int r = lane & 31, h = lane >> 5;
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
-    const v4i kf = *reinterpret_cast<const v4i*>(krow + 32 * c);
-    s = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf, qf[c], s, 0, 0, 0);
+    const int slot = (2 * c + h) ^ (r & 15);
+    const v4i kf = *reinterpret_cast<const v4i*>(kb + r * kHeadDim + 16 * slot);
+    const v4i qf = *reinterpret_cast<const v4i*>(qb + r * kHeadDim + 16 * slot);
+    s = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf, qf, s, 0, 0, 0);
   }
   return s;
 }
 
 // Per-lane constants of one wave.
 struct RowCtx {
-  int h;        // half of the wave (0/1)
-  float rowf;   // q_scale * softmax_scale * log2(e) of this lane's row
-  int t_mask;   // causal bound of this lane's row
+  int h;       // half of the wave (0/1)
+  float rowf;  // q_scale * softmax_scale * log2(e) of this lane's row
+  int t_mask;  // causal bound of this lane's row
 };
 
 // Which of the 16 score registers hold attended keys (only the last iteration
@@ -180,49 +171,57 @@ __device__ inline uint32_t key_mask(const TileBlocks& tb, int it, const RowCtx& 
   return m;
 }
 
+// Pass 1: running max of u = acc * k_scale (the row's scores up to the
+// positive factor rowf) and of z = u*rowf + log2(v_scale), whose max fixes the
+// row's largest P*v_scale.
 template <bool MASKED>
-__device__ inline float pass1_iter(const Smem& sm, const v4i (&qf)[8], int lane, const RowCtx& rc,
-                                   uint32_t kmask, float m2) {
-  const v16i s = qk_tile(sm, qf, lane);
+__device__ inline void pass1_iter(const Stage& st, const int8_t* qb, int lane, const RowCtx& rc,
+                                  uint32_t kmask, float& umax, float& zmax) {
+  const v16i s = qk_tile(st.k, qb, lane);
 #pragma unroll
   for (int i4 = 0; i4 < 4; ++i4) {
-    const float4 ks4 = *reinterpret_cast<const float4*>(sm.ks + 8 * i4 + 4 * rc.h);
-    const float4 lv4 = *reinterpret_cast<const float4*>(sm.lvs + 8 * i4 + 4 * rc.h);
+    const float4 ks4 = *reinterpret_cast<const float4*>(&st.sc[0][8 * i4 + 4 * rc.h]);
+    const float4 vs4 = *reinterpret_cast<const float4*>(&st.sc[1][8 * i4 + 4 * rc.h]);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int v = 4 * i4 + k;
-      float z = fmaf((float)s[v] * (&ks4.x)[k], rc.rowf, (&lv4.x)[k]);
-      if (MASKED) z = ((kmask >> v) & 1u) ? z : -INFINITY;
-      m2 = fmaxf(m2, z);
+      float u = (float)s[v] * (&ks4.x)[k];
+      float z = fmaf(u, rc.rowf, __builtin_amdgcn_logf((&vs4.x)[k]));
+      if (MASKED) {
+        const bool ok = (kmask >> v) & 1u;
+        u = ok ? u : -INFINITY;
+        z = ok ? z : -INFINITY;
+      }
+      umax = fmaxf(umax, u);
+      zmax = fmaxf(zmax, z);
     }
   }
-  return m2;
 }
 
+// Pass 2: P = exp2(u*rowf - Mt) <= 1, l += P, P' = P*v_scale, per-page codes,
+// fixed-point digit planes relative to the row cap (largest P'), PV.
 template <int NPL, bool MASKED>
-__device__ inline void pass2_iter(const Smem& sm, const v4i (&qf)[8], int lane, const RowCtx& rc,
-                                  uint32_t kmask, float m2, float& lsum, v16i (&acc)[NPL][8]) {
-  constexpr float kXmax = FixedPoint<NPL>::kXmax;
-  const v16i s = qk_tile(sm, qf, lane);
+__device__ inline void pass2_iter(const Stage& st, const int8_t* qb, int lane, const RowCtx& rc,
+                                  uint32_t kmask, float neg_mt, float crow, float& lsum, v16i (&acc)[NPL][8]) {
+  const v16i s = qk_tile(st.k, qb, lane);
   float pp[16];
 #pragma unroll
   for (int i4 = 0; i4 < 4; ++i4) {
-    const float4 ks4 = *reinterpret_cast<const float4*>(sm.ks + 8 * i4 + 4 * rc.h);
-    const float4 lv4 = *reinterpret_cast<const float4*>(sm.lvs + 8 * i4 + 4 * rc.h);
-    const float4 rv4 = *reinterpret_cast<const float4*>(sm.rvs + 8 * i4 + 4 * rc.h);
+    const float4 ks4 = *reinterpret_cast<const float4*>(&st.sc[0][8 * i4 + 4 * rc.h]);
+    const float4 vs4 = *reinterpret_cast<const float4*>(&st.sc[1][8 * i4 + 4 * rc.h]);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int v = 4 * i4 + k;
-      const float z = fmaf((float)s[v] * (&ks4.x)[k], rc.rowf, (&lv4.x)[k]);
-      float e = __builtin_amdgcn_exp2f(z - m2);
-      float lp = e * (&rv4.x)[k];
+      const float u = (float)s[v] * (&ks4.x)[k];
+      float p = __builtin_amdgcn_exp2f(fmaf(u, rc.rowf, neg_mt));
+      float pv = p * (&vs4.x)[k];
       if (MASKED) {
         const bool ok = (kmask >> v) & 1u;
-        e = ok ? e : 0.f;
-        lp = ok ? lp : 0.f;
+        p = ok ? p : 0.f;
+        pv = ok ? pv : 0.f;
       }
-      lsum += lp;
-      pp[v] = e;
+      lsum += p;
+      pp[v] = pv;
     }
   }
   // per-(row, page) max of P': page 0 is v = 0..7, page 1 is v = 8..15
@@ -236,8 +235,8 @@ __device__ inline void pass2_iter(const Smem& sm, const v4i (&qf)[8], int lane, 
   mx1 = xhalf_max(mx1);
   const float inv0 = mx0 > 0.f ? 127.0f / mx0 : 0.f;
   const float inv1 = mx1 > 0.f ? 127.0f / mx1 : 0.f;
-  const float f0 = mx0 * (kXmax / 127.0f);
-  const float f1 = mx1 * (kXmax / 127.0f);
+  const float f0 = mx0 * crow;  // ps * Xmax / cap of the row
+  const float f1 = mx1 * crow;
 
   v4i dig[NPL];
 #pragma unroll
@@ -256,20 +255,33 @@ __device__ inline void pass2_iter(const Smem& sm, const v4i (&qf)[8], int lane, 
     for (int p = 0; p < NPL; ++p) dig[p][w] = (int)d[p];
   }
 
-  const int8_t* vrow = sm.vt + (lane & 31) * kVStride + 16 * rc.h;
+  // V operand: 16 keys of one channel per lane, gathered by two transposing
+  // reads; slot b holds key 8(b/4) + 4h + b%4, the same key as P's byte b.
+  const int i = lane & 15;
+  const int kk = i >> 1;
+  const int key1 = 8 * (kk >> 2) + 4 * rc.h + (kk & 3);
+  const int8_t* vb = st.v;
+  const int8_t* row1 = vb + key1 * kHeadDim + 8 * (i & 1);
+  const int8_t* row2 = row1 + 16 * kHeadDim;  // key1 + 16, same swizzle
+  const int sw = key1 & 15;
+  const int half16 = (lane >> 4) & 1;
 #pragma unroll
   for (int nt = 0; nt < 8; ++nt) {
-    const v4i vf = *reinterpret_cast<const v4i*>(vrow + nt * 32 * kVStride);
+    const int slot = (2 * nt + half16) ^ sw;
+    const v2i lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32((WPA_LDS v2i*)(row1 + 16 * slot));
+    const v2i hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32((WPA_LDS v2i*)(row2 + 16 * slot));
+    const v4i vf = {lo.x, lo.y, hi.x, hi.y};
 #pragma unroll
     for (int p = 0; p < NPL; ++p) acc[p][nt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(dig[p], vf, acc[p][nt], 0, 0, 0);
   }
 }
 
 template <int NPL, int WPG, bool OUT_BF16>
-__global__ __launch_bounds__(64 * WPG, 1) void prefill_attn_kernel(AttnArgs a) {
-  constexpr int NTHR = 64 * WPG;
-  __shared__ Smem sm;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+__global__ __launch_bounds__(64 * WPG, 1) void prefill_attn_kernel(AttnArgs a, const int32_t* __restrict__ pt) {
+  __shared__ Stage st[2];
+  __shared__ alignas(16) int8_t q_lds[WPG][32 * kHeadDim];  // each wave's 32 query rows
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int rho = lane & 31;  // this lane's query row within the wave (S^T column)
 
   int u = blockIdx.x;
@@ -291,59 +303,93 @@ __global__ __launch_bounds__(64 * WPG, 1) void prefill_attn_kernel(AttnArgs a) {
   rc.t_mask = my_t < a.n_tokens ? my_t : a.n_tokens - 1;
   rc.rowf = 0.f;
 
-  // Q codes of this lane's row, in the B-operand layout (16 channels per chunk).
-  v4i qf[8];
-  {
-    const int8_t* qrow = a.q_i8 + ((long)my_t * a.n_q_heads + my_head) * kHeadDim + 16 * rc.h;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) qf[c] = row_ok ? *reinterpret_cast<const v4i*>(qrow + 32 * c) : v4i{0, 0, 0, 0};
-    if (row_ok) rc.rowf = a.q_scale[(long)my_t * a.n_q_heads + my_head] * a.row_mul;
-  }
-
   const TileBlocks tb = tile_blocks(qt, a.window_blocks, a.sink_blocks);
   const int n_it = (tb.n_total + 1) >> 1;
   const uint32_t kmask = key_mask(tb, n_it - 1, rc);
 
-  // ---- pass 1: M2 = max over attended keys of z = s*log2(e) + log2(v_scale)
-  float m2 = -INFINITY;
-  for (int it = 0; it < n_it - 1; ++it) {
-    __syncthreads();
-    stage<NTHR, false>(sm, a, tb, it, kvh);
-    __syncthreads();
-    m2 = pass1_iter<false>(sm, qf, lane, rc, 0u, m2);
-  }
-  __syncthreads();
-  stage<NTHR, false>(sm, a, tb, n_it - 1, kvh);
-  __syncthreads();
-  m2 = pass1_iter<true>(sm, qf, lane, rc, kmask, m2);
-  m2 = xhalf_max(m2);
+  // Start streaming the first pages before anything else.
+  const PagePair pg0 = page_pair(pt, tb, 0);
+  issue_stage<WPG>(st[0], a, kvh, pg0, wave, lane);
 
-  // ---- pass 2: P' = exp2(z - M2) <= 1, codes, fixed-point digits, PV
+  // This wave's 32 query rows (codes) into LDS, same chunk swizzle as K.
+  // Rows without a token or head (ragged tail, odd G) copy a valid row; their
+  // row factor is 0 and they are never stored.
+  {
+    const int s16 = lane & 15;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int r = 4 * j + (lane >> 4);
+      const int hq = head_lo + (r >> 4) < a.G ? kvh * a.G + head_lo + (r >> 4) : kvh * a.G;
+      const int tq = qt * kPage + (r & 15) < a.n_tokens ? qt * kPage + (r & 15) : a.n_tokens - 1;
+      const int8_t* src = a.q_i8 + ((long)tq * a.n_q_heads + hq) * kHeadDim + 16 * (s16 ^ (r & 15));
+      dma16(src, lds_addr(&q_lds[wave][4 * j * kHeadDim]));
+    }
+  }
+  const int8_t* qb = q_lds[wave];
+  if (row_ok) rc.rowf = a.q_scale[(long)my_t * a.n_q_heads + my_head] * a.row_mul;
+
+  // The 2*n_it steps (pass 1, then pass 2 over the same page list) alternate
+  // between the two buffers.  A step waits for its own copies, syncs (every
+  // wave is then done with the other buffer), issues the next step's copies
+  // into the other buffer, then computes on its own.
+  const int n_steps = 2 * n_it;
+  auto pages_of_step = [&](int step) { return page_pair(pt, tb, step < n_it ? step : step - n_it); };
+  PagePair pg_next = pages_of_step(1 < n_steps ? 1 : 0);
+
+  // ---- pass 1: row max of the scores and of score*log2e + log2(v_scale)
+  float umax = -INFINITY, zmax = -INFINITY;
+  int buf = 0;
+  for (int it = 0; it + 1 < n_it; ++it) {
+    wait_stage();
+    __syncthreads();
+    issue_stage<WPG>(st[buf ^ 1], a, kvh, pg_next, wave, lane);
+    pg_next = pages_of_step(it + 2);
+    pass1_iter<false>(st[buf], qb, lane, rc, 0u, umax, zmax);
+    buf ^= 1;
+  }
+  wait_stage();
+  __syncthreads();
+  issue_stage<WPG>(st[buf ^ 1], a, kvh, pg_next, wave, lane);  // pass 2, entry 0
+  pg_next = pages_of_step(n_it + 1 < n_steps ? n_it + 1 : n_it);
+  pass1_iter<true>(st[buf], qb, lane, rc, kmask, umax, zmax);
+  buf ^= 1;
+
+  umax = xhalf_max(umax);
+  zmax = xhalf_max(zmax);
+  const float mt = umax * rc.rowf;
+  const float neg_mt = -mt;
+  // cap = largest P' of the row (with P = exp2(score*log2e - Mt) <= 1); the
+  // small factor covers rounding between the two passes
+  const float cap = __builtin_amdgcn_exp2f(zmax - mt) * (1.0f + 1.0f / 4096.0f);
+  constexpr float kXmax = FixedPoint<NPL>::kXmax;
+  const float crow = kXmax / (127.0f * cap);
+
+  // ---- pass 2
   v16i acc[NPL][8];
 #pragma unroll
   for (int p = 0; p < NPL; ++p)
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) acc[p][nt] = v16i{};
   float lsum = 0.f;
-  for (int it = 0; it < n_it - 1; ++it) {
+  for (int it = 0; it + 1 < n_it; ++it) {
+    wait_stage();
     __syncthreads();
-    stage<NTHR, true>(sm, a, tb, it, kvh);
-    __syncthreads();
-    pass2_iter<NPL, false>(sm, qf, lane, rc, 0u, m2, lsum, acc);
+    issue_stage<WPG>(st[buf ^ 1], a, kvh, pg_next, wave, lane);
+    if (n_it + it + 2 < n_steps) pg_next = pages_of_step(n_it + it + 2);
+    pass2_iter<NPL, false>(st[buf], qb, lane, rc, 0u, neg_mt, crow, lsum, acc);
+    buf ^= 1;
   }
+  wait_stage();
   __syncthreads();
-  stage<NTHR, true>(sm, a, tb, n_it - 1, kvh);
-  __syncthreads();
-  pass2_iter<NPL, true>(sm, qf, lane, rc, kmask, m2, lsum, acc);
+  pass2_iter<NPL, true>(st[buf], qb, lane, rc, kmask, neg_mt, crow, lsum, acc);
 
-  // ---- epilogue: recombine digit planes, divide by Xmax * l, store
-  constexpr float kXmax = FixedPoint<NPL>::kXmax;
+  // ---- epilogue: recombine digit planes, scale by cap / (Xmax * l), store
   lsum = xhalf_sum(lsum);
-  const float rinv = 1.0f / (kXmax * lsum);
+  const float rscale = cap / (kXmax * lsum);
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
     const int r = 8 * (v >> 2) + 4 * rc.h + (v & 3);  // output row of register v
-    const float rr = __shfl(rinv, r);
+    const float rr = __shfl(rscale, r);
     const int hig = head_lo + (r >> 4);
     const int t = qt * kPage + (r & 15);
     if (hig >= a.G || t >= a.n_tokens) continue;
@@ -368,9 +414,11 @@ __global__ __launch_bounds__(64 * WPG, 1) void prefill_attn_kernel(AttnArgs a) {
 template <int WPG>
 static void launch_wpg(const AttnArgs& a, bool out_bf16, unsigned grid, hipStream_t stream) {
   if (out_bf16)
-    hipLaunchKernelGGL((prefill_attn_kernel<WPA_NPL, WPG, true>), dim3(grid), dim3(64 * WPG), 0, stream, a);
+    hipLaunchKernelGGL((prefill_attn_kernel<WPA_NPL, WPG, true>), dim3(grid), dim3(64 * WPG), 0, stream, a,
+                       a.page_table);
   else
-    hipLaunchKernelGGL((prefill_attn_kernel<WPA_NPL, WPG, false>), dim3(grid), dim3(64 * WPG), 0, stream, a);
+    hipLaunchKernelGGL((prefill_attn_kernel<WPA_NPL, WPG, false>), dim3(grid), dim3(64 * WPG), 0, stream, a,
+                       a.page_table);
 }
 
 hipError_t launch_prefill_attn(const AttnArgs& args_in, bool out_bf16, hipStream_t stream) {
