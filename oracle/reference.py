@@ -206,8 +206,14 @@ def _quantize_p_block(pv: np.ndarray, with_ties: bool = False):
     p32 = pv.astype(np.float32)
     mx = p32.max(axis=1)
     nz = mx > 0
-    inv = (np.float32(127.0) / np.where(nz, mx, np.float32(1.0))).astype(np.float32)
-    x = (p32 * inv[:, None]).astype(np.float32)
+    # The code depends only on P'/max.  Blocks whose max is so small that
+    # 127/max would overflow float32 are first scaled by 2^64 (exact).
+    tiny = nz & (mx < np.float32(2.0 ** -60))
+    up = np.where(tiny, np.float32(2.0 ** 64), np.float32(1.0)).astype(np.float32)
+    p32s = (p32 * up[:, None]).astype(np.float32)
+    mxs = (mx * up).astype(np.float32)
+    inv = (np.float32(127.0) / np.where(nz, mxs, np.float32(1.0))).astype(np.float32)
+    x = (p32s * inv[:, None]).astype(np.float32)
     codes = np.clip(np.rint(x), -127, 127)
     codes[~nz] = 0.0
     ps = np.where(nz, mx.astype(np.float64) / 127.0, 0.0)

@@ -306,3 +306,14 @@ def test_mirror_tie_slack_is_small_on_random_inputs():
     assert np.mean(slack) < 1e-4 * mo
     assert np.median(slack) == 0.0
     assert np.mean(slack[200:] > 0) < 0.4
+
+
+def test_p_block_codes_for_tiny_block_max():
+    """Codes depend only on P'/max: a block scaled by 2^-124 (still a normal
+    float32, but 127/max overflows) keeps the codes of the unscaled block."""
+    from oracle.reference import _quantize_p_block
+    pv = np.array([[0.5, 0.25, 0.125, 0.0]])
+    c1, ps1 = _quantize_p_block(pv)
+    c2, ps2 = _quantize_p_block(pv * 2.0 ** -124)
+    assert np.array_equal(c1, c2)
+    assert np.all(np.isfinite(c2)) and ps2[0] > 0

@@ -202,7 +202,8 @@ __device__ inline void pass1_iter(const Stage& st, const int8_t* qb, int lane, c
 // fixed-point digit planes relative to the row cap (largest P'), PV.
 template <int NPL, bool MASKED>
 __device__ inline void pass2_iter(const Stage& st, const int8_t* qb, int lane, const RowCtx& rc,
-                                  uint32_t kmask, float neg_mt, float crow, float& lsum, v16i (&acc)[NPL][8]) {
+                                  uint32_t kmask, float neg_mt, float crow, float cap, float& lsum,
+                                  v16i (&acc)[NPL][8]) {
   const v16i s = qk_tile(st.k, qb, lane);
   float pp[16];
 #pragma unroll
@@ -233,8 +234,11 @@ __device__ inline void pass2_iter(const Stage& st, const int8_t* qb, int lane, c
   }
   mx0 = xhalf_max(mx0);
   mx1 = xhalf_max(mx1);
-  const float inv0 = mx0 > 0.f ? 127.0f / mx0 : 0.f;
-  const float inv1 = mx1 > 0.f ? 127.0f / mx1 : 0.f;
+  // A block whose largest P' is below 2^-60 of the row cap weighs nothing at
+  // this fixed-point resolution: its codes are irrelevant (and 127/mx could
+  // overflow), so they are set to 0.
+  const float inv0 = mx0 > 0x1p-60f * cap ? 127.0f / mx0 : 0.f;
+  const float inv1 = mx1 > 0x1p-60f * cap ? 127.0f / mx1 : 0.f;
   const float f0 = mx0 * crow;  // ps * Xmax / cap of the row
   const float f1 = mx1 * crow;
 
@@ -376,12 +380,12 @@ __global__ __launch_bounds__(64 * WPG, 1) void prefill_attn_kernel(AttnArgs a, c
     __syncthreads();
     issue_stage<WPG>(st[buf ^ 1], a, kvh, pg_next, wave, lane);
     if (n_it + it + 2 < n_steps) pg_next = pages_of_step(n_it + it + 2);
-    pass2_iter<NPL, false>(st[buf], qb, lane, rc, 0u, neg_mt, crow, lsum, acc);
+    pass2_iter<NPL, false>(st[buf], qb, lane, rc, 0u, neg_mt, crow, cap, lsum, acc);
     buf ^= 1;
   }
   wait_stage();
   __syncthreads();
-  pass2_iter<NPL, true>(st[buf], qb, lane, rc, kmask, neg_mt, crow, lsum, acc);
+  pass2_iter<NPL, true>(st[buf], qb, lane, rc, kmask, neg_mt, crow, cap, lsum, acc);
 
   // ---- epilogue: recombine digit planes, scale by cap / (Xmax * l), store
   lsum = xhalf_sum(lsum);
