@@ -19,7 +19,7 @@ struct AttnArgs {
   int window_blocks, sink_blocks;
   float softmax_scale;
   // filled in by the launcher
-  int G, n_pairs, hgroups, n_tiles;
+  int G, hgroups, n_tiles;
   float row_mul;
 };
 
