@@ -34,12 +34,21 @@ namespace wpa {
 typedef int v2i __attribute__((ext_vector_type(2)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 #define WPA_LDS __attribute__((address_space(3)))
+#define WPA_CONST __attribute__((address_space(4)))
 
 constexpr int kStepKeys = 64;                 // keys per step (four pages)
 constexpr int kStage = kStepKeys * kHeadDim;  // bytes of one staged K or V tile
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kMagic = 8388608.0f;  // 2^23: x + 2^23 holds the integer x in its low 23 bits
-constexpr float kXmax = 32512.f;      // fixed-point full scale: (x + 128) >> 8 stays <= 127
+constexpr int kKeysPerGroup = 4;              // keys (rows) of one 1 KB copy group
+constexpr float kTwo23 = 8388608.0f;  // 2^23 + v rounds v to an integer held in the low mantissa bits
+// Fixed point of the PV weights: full scale Xmax = 127 * 256, relative to a
+// cap that bounds every P' of the row (P' <= 1 up to exp2/log2 rounding).
+constexpr float kXmax = 32512.f;
+constexpr float kCap = 1.0f + 1.0f / 4096.0f;
+// F = rint(f * 2^16) with f = mx * Xmax / (127 * cap) = mx * 256 / cap
+constexpr float kFScale = 16777216.0f / kCap;
+constexpr uint32_t kDigitBias = (128u << 16) + (1u << 15);  // digit offset 128, rounding half
+constexpr float kTiny = 0x1p-60f;
 
 // One stage buffer.  K and V tiles are row-major (row = key of the step, 256
 // bytes) with the 16-byte chunk c of row r stored in slot c ^ swz(r), so the
@@ -82,24 +91,24 @@ __device__ inline float rows_sum(float x) {
   return x + y;
 }
 
-// Physical pages of list entries 4s .. 4s+3, branch-free (entries past the
-// end clamp to the last one; their keys are masked).  Entry li is block li
-// for the sink part and win_start + li - n_sink after it.
+// Physical pages of list entries 4s .. 4s+3, read through the scalar cache
+// (entries past the end clamp to the last one; their keys are masked).  Entry
+// li is block li for the sink part and win_start + li - n_sink after it.
 struct Pages {
   int p[4];
 };
-__device__ inline Pages step_pages(const int32_t* __restrict__ pt, const TileBlocks& tb, int step) {
+__device__ inline Pages step_pages(const WPA_CONST int32_t* pt, const TileBlocks& tb, int step) {
   Pages pg;
   const int li0 = 4 * step;
   const int shift = tb.win_start - tb.n_sink;
   if (li0 + 3 < tb.n_total && (li0 >= tb.n_sink || li0 + 3 < tb.n_sink)) {
     // four consecutive blocks: one 16-byte scalar load
     const int b0 = li0 + (li0 >= tb.n_sink ? shift : 0);
-    const int4 v = *reinterpret_cast<const int4*>(pt + b0);
-    pg.p[0] = v.x;
-    pg.p[1] = v.y;
-    pg.p[2] = v.z;
-    pg.p[3] = v.w;
+    const v4i v = *reinterpret_cast<const WPA_CONST v4i*>(pt + b0);
+    pg.p[0] = v[0];
+    pg.p[1] = v[1];
+    pg.p[2] = v[2];
+    pg.p[3] = v[3];
   } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -114,40 +123,57 @@ __device__ inline Pages step_pages(const int32_t* __restrict__ pt, const TileBlo
 // land at lds_base + 16*l (4*l).  Issued as inline assembly so the compiler
 // does not model the in-flight LDS write; the kernel orders it explicitly
 // with wait_stage() and a workgroup barrier before any read of that buffer.
+// The 16-byte form takes a scalar base address and a 32-bit per-lane offset.
 __device__ inline uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const WPA_LDS void*)p;
 }
-__device__ inline void dma16(const void* src, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_base) : "memory", "m0");
+__device__ inline void dma16(uint32_t voff, const int8_t* sbase, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_base)
+               : "memory", "m0");
 }
 __device__ inline void dma4(const void* src, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(lds_base) : "memory", "m0");
 }
 __device__ inline void wait_stage() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Issue the copies of one step's four pages: 16 K (and, for pass 2, 16 V)
-// row groups of 4 rows (1 KB, one 16-byte chunk per lane) shared over the
-// waves, plus the 64 K and 64 V scales.
-template <int WPG, bool WITH_V>
-__device__ inline void issue_stage(Stage& st, const AttnArgs& a, int kvh, const Pages& pg, int wave, int lane) {
-  const long row_bytes = (long)a.n_kv_heads * kHeadDim;
-  const long page_bytes = kPage * row_bytes;
+// Row groups of 4 keys (1 KB of one page, one 16-byte chunk per lane) that a
+// wave copies each step: g = wave + WPG*j for j < 16/WPG (K; V uses the same
+// g + 16).  Their in-page byte offsets are per-lane constants, kept in
+// registers so a copy costs no vector arithmetic.
+template <int WPG>
+struct DmaPlan {
+  static constexpr int NJ = 16 / WPG;
+  uint32_t voff[NJ];
+};
+template <int WPG>
+__device__ inline void make_plan(DmaPlan<WPG>& pl, int row_bytes, int kvh, int wave, int lane) {
   const int q = lane >> 4, s = lane & 15;
 #pragma unroll
-  for (int j = 0; j < (WITH_V ? 32 : 16) / WPG; ++j) {
-    // row group g = wave + WPG*j (wave < WPG): its page and K/V choice depend
-    // only on j, so both are compile-time after unrolling
-    const int page = ((WPG * j) >> 2) & 3;
-    const bool isv = WPG * j >= 16;
+  for (int j = 0; j < DmaPlan<WPG>::NJ; ++j) {
     const int g = wave + WPG * j;
-    const int rr = 4 * (g & 3) + q;  // row inside the page
-    const int r = 16 * page + rr;    // row of the tile
-    const int8_t* src = (isv ? a.v_pool : a.k_pool) + (long)pg.p[page] * page_bytes +
-                        ((long)rr * row_bytes + (long)kvh * kHeadDim + 16 * (s ^ swz(r)));
-    dma16(src, lds_addr((isv ? st.v : st.k) + 4 * (g & 15) * kHeadDim));
+    const int page = (WPG * j) >> 2;  // WPG divides 4, so this is g / 4
+    const int rr = 4 * (g & 3) + q;   // row inside the page
+    const int r = 16 * page + rr;     // row of the tile
+    pl.voff[j] = (uint32_t)(rr * row_bytes + kvh * kHeadDim + 16 * (s ^ swz(r)));
   }
-  // k_scale by wave 0, v_scale by wave 1 (both by wave 0 when WPG == 1)
-  // page of key `lane` (row group q), selected with bit operations only
+}
+
+// Issue the copies of one step's four pages: K (and, for pass 2, V) row groups
+// shared over the waves, plus the 64 K and 64 V scales.
+template <int WPG, bool WITH_V>
+__device__ inline void issue_stage(Stage& st, const AttnArgs& a, const DmaPlan<WPG>& pl, long page_bytes, int kvh,
+                                   const Pages& pg, int wave, int lane) {
+#pragma unroll
+  for (int j = 0; j < DmaPlan<WPG>::NJ; ++j) {
+    const int page = (WPG * j) >> 2;
+    const int g = wave + WPG * j;
+    const long pbase = (long)pg.p[page] * page_bytes;
+    dma16(pl.voff[j], a.k_pool + pbase, lds_addr(st.k + kKeysPerGroup * kHeadDim * g));
+    if (WITH_V) dma16(pl.voff[j], a.v_pool + pbase, lds_addr(st.v + kKeysPerGroup * kHeadDim * g));
+  }
+  // k_scale by wave 0, v_scale by wave 1 (both by wave 0 when WPG == 1):
+  // lane l copies the scale of key l, page l/16
+  const int q = lane >> 4, s = lane & 15;
   const int odd = -(q & 1), high = -((q >> 1) & 1);
   const int lo = pg.p[0] ^ ((pg.p[0] ^ pg.p[1]) & odd);
   const int hi = pg.p[2] ^ ((pg.p[2] ^ pg.p[3]) & odd);
@@ -199,13 +225,14 @@ __device__ inline uint32_t key_mask(const TileBlocks& tb, int step, const RowCtx
   return m;
 }
 
-// Pass 1: running max of u = acc * k_scale (the score up to the positive
-// factor rowf) and of z = u*rowf + log2(v_scale), whose max fixes the row's
-// largest P*v_scale.  Each lane takes one log2 (key = lane) and the wave
-// shares them through its own LDS slice.
+// Pass 1: running max of z = score*log2(e) + log2(v_scale) = (acc*k_scale)*rowf
+// + log2(v_scale).  Its row maximum Z makes P' = exp2(z - Z) <= 1 in pass 2,
+// so the row's largest P' is 1 and fixes the fixed-point scale.  Each lane
+// takes one log2 (key = lane) and the wave shares them through its own LDS
+// slice.
 template <bool MASKED>
 __device__ inline void pass1_step(const Stage& st, float* lvs_w, const v4i (&qf)[4], int lane, const RowCtx& rc,
-                                  uint32_t kmask, float& umax, float& zmax) {
+                                  uint32_t kmask, float& zmax) {
   lvs_w[lane] = __builtin_amdgcn_logf(st.sc[1][lane]);
   v4i s[4];
   qk_step(st.k, qf, lane, s);
@@ -214,36 +241,28 @@ __device__ inline void pass1_step(const Stage& st, float* lvs_w, const v4i (&qf)
   for (int p = 0; p < 4; ++p) {
     const float4 ks4 = *reinterpret_cast<const float4*>(&st.sc[0][16 * p + 4 * rc.g]);
     const float4 lv4 = *reinterpret_cast<const float4*>(&lvs_w[16 * p + 4 * rc.g]);
+    float z[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float u = (float)s[p][i] * (&ks4.x)[i];
-      float z = fmaf(u, rc.rowf, (&lv4.x)[i]);
-      if (MASKED) {
-        const bool ok = (kmask >> (4 * p + i)) & 1u;
-        u = ok ? u : -INFINITY;
-        z = ok ? z : -INFINITY;
-      }
-      umax = fmaxf(umax, u);
-      zmax = fmaxf(zmax, z);
+      z[i] = fmaf((float)s[p][i] * (&ks4.x)[i], rc.rowf, (&lv4.x)[i]);
+      if (MASKED) z[i] = ((kmask >> (4 * p + i)) & 1u) ? z[i] : -INFINITY;
     }
+    zmax = fmaxf(fmaxf(zmax, fmaxf(z[0], z[1])), fmaxf(z[2], z[3]));
   }
   __builtin_amdgcn_wave_barrier();
 }
 
-// Byte k of four words into one word (v_perm_b32 selectors: 0-3 pick bytes
-// of the second operand, 4-7 of the first, 0x0c gives zero).
-__device__ inline uint32_t gather_byte0(uint32_t y0, uint32_t y1, uint32_t y2, uint32_t y3) {
-  return __builtin_amdgcn_perm(y1, y0, 0x0c0c0400u) | __builtin_amdgcn_perm(y3, y2, 0x04000c0cu);
-}
-__device__ inline uint32_t gather_byte1(uint32_t y0, uint32_t y1, uint32_t y2, uint32_t y3) {
-  return __builtin_amdgcn_perm(y1, y0, 0x0c0c0501u) | __builtin_amdgcn_perm(y3, y2, 0x05010c0cu);
-}
-
-// Pass 2: P = exp2(u*rowf - Mt) <= 1, l += P, P' = P*v_scale, per-page codes,
-// fixed-point digit planes relative to the row cap (largest P'), PV.
+// Pass 2: e = exp2(z - Z - log2 v_scale) = P, l += P, P' = P * v_scale <= 1,
+// per-page codes code = rint(P' * 127 / max P'), their weights ps * code as
+// the fixed-point integer x = rint(code * f), f = max P' * Xmax / (127 * cap),
+// split into two signed int8 digit planes x = d0 + 256 d1, then PV.
+//
+// code * f is formed as (code * F + 2^15) >> 16 with F = rint(f * 2^16) < 2^24
+// by one 24-bit multiply-add; with a bias of 128 in the upper half, bytes 2
+// and 3 of the result are d0 + 128 and d1.
 template <bool MASKED>
 __device__ inline void pass2_step(const Stage& st, const v4i (&qf)[4], int lane, const RowCtx& rc, uint32_t kmask,
-                                  float neg_mt, float crow, float tiny, float& lsum, v4i (&acc)[2][16]) {
+                                  float neg_z, float& lsum, v4i (&acc)[2][16]) {
   v4i s[4];
   qk_step(st.k, qf, lane, s);
   float pp[4][4];
@@ -254,8 +273,7 @@ __device__ inline void pass2_step(const Stage& st, const v4i (&qf)[4], int lane,
     const float4 vs4 = *reinterpret_cast<const float4*>(&st.sc[1][16 * p + 4 * rc.g]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float u = (float)s[p][i] * (&ks4.x)[i];
-      float e = __builtin_amdgcn_exp2f(fmaf(u, rc.rowf, neg_mt));
+      float e = __builtin_amdgcn_exp2f(fmaf((float)s[p][i] * (&ks4.x)[i], rc.rowf, neg_z));
       float pv = e * (&vs4.x)[i];
       if (MASKED) {
         const bool ok = (kmask >> (4 * p + i)) & 1u;
@@ -291,17 +309,19 @@ __device__ inline void pass2_step(const Stage& st, const v4i (&qf)[4], int lane,
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     // pages weighing below 2^-60 of the cap round to zero in this fixed point
-    const float inv = mx[p] > tiny ? 127.0f * __builtin_amdgcn_rcpf(mx[p]) : 0.f;
-    const float f = mx[p] * crow;  // ps * Xmax / cap
-    uint32_t y[4], z[4];
+    const bool live = mx[p] > kTiny;
+    const float inv = live ? 127.0f * __builtin_amdgcn_rcpf(mx[p]) : 0.f;
+    const uint32_t F = (uint32_t)fmaf(mx[p], kFScale, 0.5f);
+    uint32_t r[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float code = rintf(pp[p][i] * inv);
-      y[i] = __float_as_uint(fmaf(code, f, kMagic));  // 2^23 + x
-      z[i] = y[i] + 128u;
+      const uint32_t code = __float_as_uint(fmaf(pp[p][i], inv, kTwo23));  // 2^23 + rint(P' * inv)
+      r[i] = __umul24(code, F) + kDigitBias;
     }
-    dig[0][p] = (int)gather_byte0(y[0], y[1], y[2], y[3]);  // low digit, signed
-    dig[1][p] = (int)gather_byte1(z[0], z[1], z[2], z[3]);  // high digit (x + 128) >> 8
+    const uint32_t w01 = __builtin_amdgcn_perm(r[1], r[0], 0x07060302u);
+    const uint32_t w23 = __builtin_amdgcn_perm(r[3], r[2], 0x07060302u);
+    dig[0][p] = (int)(__builtin_amdgcn_perm(w23, w01, 0x06040200u) ^ 0x80808080u);  // low digit, signed
+    dig[1][p] = (int)__builtin_amdgcn_perm(w23, w01, 0x07050301u);                 // high digit
   }
 
   // V operand: lane (row g, column j) needs 16 keys of channel 16nt + j in the
@@ -325,9 +345,10 @@ __device__ inline void pass2_step(const Stage& st, const v4i (&qf)[4], int lane,
 }
 
 template <int WPG, bool OUT_BF16>
-__global__ __launch_bounds__(64 * WPG, 2) void prefill_attn_kernel(AttnArgs a, const int32_t* __restrict__ pt) {
+__global__ __launch_bounds__(64 * WPG, 2) void prefill_attn_kernel(AttnArgs a, const int32_t* __restrict__ pt_arg) {
   __shared__ Stage st[2];
   __shared__ alignas(16) float lvs[WPG][kStepKeys];  // per-wave log2(v_scale) of the step
+  const WPA_CONST int32_t* pt = (const WPA_CONST int32_t*)pt_arg;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
@@ -349,9 +370,14 @@ __global__ __launch_bounds__(64 * WPG, 2) void prefill_attn_kernel(AttnArgs a, c
   const int n_st = (tb.n_total + 3) >> 2;
   const uint32_t kmask = key_mask(tb, n_st - 1, rc);
 
+  const int row_bytes = a.n_kv_heads * kHeadDim;
+  const long page_bytes = (long)kPage * row_bytes;
+  DmaPlan<WPG> plan;
+  make_plan<WPG>(plan, row_bytes, kvh, wave, lane);
+
   // Start streaming the first pages before anything else.
   const Pages pg0 = step_pages(pt, tb, 0);
-  issue_stage<WPG, false>(st[0], a, kvh, pg0, wave, lane);
+  issue_stage<WPG, false>(st[0], a, plan, page_bytes, kvh, pg0, wave, lane);
 
   // Q codes of this lane's row in the B-operand layout (16 channels per chunk);
   // rows past the end read the last token and are never stored.
@@ -373,33 +399,25 @@ __global__ __launch_bounds__(64 * WPG, 2) void prefill_attn_kernel(AttnArgs a, c
   Pages pg_next = pages_of(1 < n_all ? 1 : 0);
   float* lvs_w = lvs[wave];
 
-  // ---- pass 1: row max of the scores and of score*log2e + log2(v_scale)
-  float umax = -INFINITY, zmax = -INFINITY;
+  // ---- pass 1: row max of score*log2e + log2(v_scale)
+  float zmax = -INFINITY;
   int buf = 0;
   for (int it = 0; it + 1 < n_st; ++it) {
     wait_stage();
     __syncthreads();
-    issue_stage<WPG, false>(st[buf ^ 1], a, kvh, pg_next, wave, lane);
+    issue_stage<WPG, false>(st[buf ^ 1], a, plan, page_bytes, kvh, pg_next, wave, lane);
     pg_next = pages_of(it + 2);
-    pass1_step<false>(st[buf], lvs_w, qf, lane, rc, 0u, umax, zmax);
+    pass1_step<false>(st[buf], lvs_w, qf, lane, rc, 0u, zmax);
     buf ^= 1;
   }
   wait_stage();
   __syncthreads();
-  issue_stage<WPG, true>(st[buf ^ 1], a, kvh, pg_next, wave, lane);  // pass 2, first step
+  issue_stage<WPG, true>(st[buf ^ 1], a, plan, page_bytes, kvh, pg_next, wave, lane);  // pass 2, first step
   pg_next = pages_of(n_st + 1 < n_all ? n_st + 1 : n_st);
-  pass1_step<true>(st[buf], lvs_w, qf, lane, rc, kmask, umax, zmax);
+  pass1_step<true>(st[buf], lvs_w, qf, lane, rc, kmask, zmax);
   buf ^= 1;
 
-  umax = rows_max(umax);
-  zmax = rows_max(zmax);
-  const float mt = umax * rc.rowf;
-  const float neg_mt = -mt;
-  // cap = largest P' of the row (with P = exp2(score*log2e - Mt) <= 1); the
-  // small factor covers rounding between the two passes
-  const float cap = __builtin_amdgcn_exp2f(zmax - mt) * (1.0f + 1.0f / 4096.0f);
-  const float crow = kXmax / (127.0f * cap);
-  const float tiny = 0x1p-60f * cap;
+  const float neg_z = -rows_max(zmax);
 
   // ---- pass 2
   v4i acc[2][16];
@@ -411,19 +429,19 @@ __global__ __launch_bounds__(64 * WPG, 2) void prefill_attn_kernel(AttnArgs a, c
   for (int it = 0; it + 1 < n_st; ++it) {
     wait_stage();
     __syncthreads();
-    issue_stage<WPG, true>(st[buf ^ 1], a, kvh, pg_next, wave, lane);
+    issue_stage<WPG, true>(st[buf ^ 1], a, plan, page_bytes, kvh, pg_next, wave, lane);
     if (n_st + it + 2 < n_all) pg_next = pages_of(n_st + it + 2);
-    pass2_step<false>(st[buf], qf, lane, rc, 0u, neg_mt, crow, tiny, lsum, acc);
+    pass2_step<false>(st[buf], qf, lane, rc, 0u, neg_z, lsum, acc);
     buf ^= 1;
   }
   wait_stage();
   __syncthreads();
-  pass2_step<true>(st[buf], qf, lane, rc, kmask, neg_mt, crow, tiny, lsum, acc);
+  pass2_step<true>(st[buf], qf, lane, rc, kmask, neg_z, lsum, acc);
 
   // ---- epilogue: recombine the digit planes, scale by cap / (Xmax * l), store.
   // Output register i of tile nt is row 4g + i, channel 16nt + lane%16.
   lsum = rows_sum(lsum);
-  const float rscale = cap / (kXmax * lsum);
+  const float rscale = kCap / (kXmax * lsum);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = 4 * rc.g + i;
