@@ -51,11 +51,11 @@ constexpr uint32_t kDigitBias = (128u << 16) + (1u << 15);  // digit offset 128,
 constexpr float kTiny = 0x1p-60f;
 
 // One stage buffer.  K and V tiles are row-major (row = key of the step, 256
-// bytes) with the 16-byte chunk c of row r stored in slot c ^ swz(r), so the
-// operand reads below touch every bank once per 16 lanes: the K reads see 16
-// consecutive rows of one page, the transposing V reads 4 rows of each of two
-// pages 16 rows apart.
-__device__ inline int swz(int r) { return (r & 15) ^ (((r >> 4) & 3) << 2); }
+// bytes) with the 16-byte chunk c of row r stored in slot c ^ swz(r).  The
+// operand reads below then touch every bank once per half wave: the K reads
+// see 16 consecutive rows of one page (slots r%16 ^ const), the transposing V
+// reads rows 8h..8h+7 and 16+8h..16+8h+7 (slots m and 8 + m).
+__device__ inline int swz(int r) { return (r & 15) ^ (((r >> 4) & 1) << 3); }
 struct alignas(16) Stage {
   int8_t k[kStage];
   int8_t v[kStage];
