@@ -100,7 +100,10 @@ wpa_status wpa_quantize_q_rows(const void* q, wpa_dtype q_dtype, int n_tokens, i
  *                  Entries must lie in [0, n_pool_pages); this is a caller
  *                  precondition and is not checked on the device.
  *   out            [n_tokens][n_q_heads][256], out_dtype WPA_BF16 (rounded to
- *                  nearest even) or WPA_F32.
+ *                  nearest even) or WPA_F32.  The call enqueues two kernels;
+ *                  the first leaves a per-row float in the first four bytes of
+ *                  each output row, which the second reads and overwrites, so
+ *                  out must not alias any input.
  * Errors: NULL pointer -> WPA_ERR_NULL; n_tokens < 0, heads <= 0,
  * n_q_heads % n_kv_heads != 0, n_pool_pages < ceil(n_tokens/16),
  * sink_blocks < 0, softmax_scale not finite or <= 0 -> WPA_ERR_SHAPE;

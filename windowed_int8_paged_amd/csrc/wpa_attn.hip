@@ -9,22 +9,30 @@
 // <= 0 is full causal attention).
 //
 // gfx950 design
+//   * Two launches over the same per-tile key list.  The first (row max)
+//     computes QK^T and the row maximum Z of score*log2(e) + log2(v_scale)
+//     for every (query row, head) and parks it in the first four bytes of that
+//     row's output; the second (attention) recomputes QK^T, forms P codes and
+//     runs PV.  Knowing Z before any weight is formed makes the row's largest
+//     P*v_scale exactly 1, which fixes the fixed-point scale below.
 //   * One workgroup = one 16-token query tile x one KV head x up to 4 of its
-//     query heads, one wave per head (16 query rows).  A wave needs at most
-//     256 registers, so two waves share each SIMD and the hardware overlaps
-//     one wave's matrix work with the other's vector work.
+//     query heads.  In the attention launch a wave takes one head (16 query
+//     rows) and needs at most 256 registers, so two waves share each SIMD; in
+//     the row-max launch a wave takes two heads and half of the keys, so each
+//     K fragment read from LDS feeds two products, and four waves share a SIMD.
 //   * Scores are computed transposed, S^T = K . Q^T, with
 //     v_mfma_i32_16x16x64_i8 per 16-key page: a lane holds 4 keys of one query
-//     row per page, so row reductions are in-lane plus two lane swaps.
+//     row per page, so row reductions are in-lane plus lane swaps.
 //   * A step covers 64 keys (four pages).  P codes are exactly the
 //     per-(row, 16-key block) int8 codes of the method; their weights ps*code
 //     are written as one fixed-point integer relative to the row's largest
-//     P*v_scale (found by a first QK pass) and split into two signed int8
-//     digit planes, so PV runs at the full K = 64 rate with int32 accumulation
-//     across every block and no per-block floating-point rescale.
-//   * K and V pages go global -> LDS by asynchronous LDS DMA into row-major
-//     XOR-swizzled tiles, double-buffered; V operands are gathered with the
-//     transposing read ds_read_b64_tr_b8.
+//     P*v_scale and split into two signed int8 digit planes, so PV runs at the
+//     full K = 64 rate with int32 accumulation across every block and no
+//     per-block floating-point rescale.
+//   * K and V pages go global -> LDS by asynchronous LDS DMA (each wave copies
+//     whole pages) into row-major XOR-swizzled tiles, double-buffered; LDS
+//     fragment reads are software-pipelined ahead of their matrix products;
+//     V operands are gathered with the transposing read ds_read_b64_tr_b8.
 
 #include "wpa_common.h"
 #include "wpa_launch.h"
@@ -56,10 +64,16 @@ constexpr float kTiny = 0x1p-60f;
 // see 16 consecutive rows of one page (slots r%16 ^ const), the transposing V
 // reads rows 8h..8h+7 and 16+8h..16+8h+7 (slots m and 8 + m).
 __device__ inline int swz(int r) { return (r & 15) ^ (((r >> 4) & 1) << 3); }
+// Scales of page p of the step: sc[p][0..15] k_scale, sc[p][16..31] v_scale
+// of its 16 keys (one 256-byte copy per page; slots 32..63 repeat them).
 struct alignas(16) Stage {
   int8_t k[kStage];
   int8_t v[kStage];
-  float sc[2][kStepKeys];  // [k_scale, v_scale][key]
+  float sc[4][64];
+};
+struct alignas(16) StageK {  // the row-max launch stages no V
+  int8_t k[kStage];
+  float sc[4][64];
 };
 
 // ---- cross-lane helpers: rows of 16 lanes R0..R3
@@ -91,30 +105,21 @@ __device__ inline float rows_sum(float x) {
   return x + y;
 }
 
-// Physical pages of list entries 4s .. 4s+3, read through the scalar cache
-// (entries past the end clamp to the last one; their keys are masked).  Entry
-// li is block li for the sink part and win_start + li - n_sink after it.
-struct Pages {
-  int p[4];
+// Each wave copies 4/WPG whole pages of a step: list entries
+// 4s + wave*PPW + i.  Their physical pages are read through the scalar cache
+// (entries past the end clamp to the last one; their keys are masked).
+template <int WPG>
+struct WavePages {
+  static constexpr int PPW = 4 / WPG;
+  int p[PPW];
 };
-__device__ inline Pages step_pages(const WPA_CONST int32_t* pt, const TileBlocks& tb, int step) {
-  Pages pg;
-  const int li0 = 4 * step;
-  const int shift = tb.win_start - tb.n_sink;
-  if (li0 + 3 < tb.n_total && (li0 >= tb.n_sink || li0 + 3 < tb.n_sink)) {
-    // four consecutive blocks: one 16-byte scalar load
-    const int b0 = li0 + (li0 >= tb.n_sink ? shift : 0);
-    const v4i v = *reinterpret_cast<const WPA_CONST v4i*>(pt + b0);
-    pg.p[0] = v[0];
-    pg.p[1] = v[1];
-    pg.p[2] = v[2];
-    pg.p[3] = v[3];
-  } else {
+template <int WPG>
+__device__ inline WavePages<WPG> wave_pages(const WPA_CONST int32_t* pt, const TileBlocks& tb, int step, int wave) {
+  WavePages<WPG> pg;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int li = min(li0 + i, tb.n_total - 1);
-      pg.p[i] = pt[li + (li >= tb.n_sink ? shift : 0)];
-    }
+  for (int i = 0; i < WavePages<WPG>::PPW; ++i) {
+    const int li = min(4 * step + wave * WavePages<WPG>::PPW + i, tb.n_total - 1);
+    pg.p[i] = pt[tb.block(li)];
   }
   return pg;
 }
@@ -134,77 +139,66 @@ __device__ inline void dma16(uint32_t voff, const int8_t* sbase, uint32_t lds_ba
 __device__ inline void dma4(const void* src, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(lds_base) : "memory", "m0");
 }
-__device__ inline void wait_stage() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// vmcnt(0) through the builtin, so the compiler's own wait tracking sees it:
+// registers filled by earlier vector loads (Q codes, scales) then count as
+// ready, and no wait on the in-flight copies is inserted before their uses.
+__device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+__device__ inline void wait_stage() {
+  asm volatile("" ::: "memory");
+  wait_vmem();
+  asm volatile("" ::: "memory");
+}
 
-// Row groups of 4 keys (1 KB of one page, one 16-byte chunk per lane) that a
-// wave copies each step: g = wave + WPG*j for j < 16/WPG (K; V uses the same
-// g + 16).  Their in-page byte offsets are per-lane constants, kept in
-// registers so a copy costs no vector arithmetic.
+// A wave's copies per step: for each of its pages, four 1 KB row groups
+// (keys 4j .. 4j+3, one 16-byte chunk per lane) of K (and V), and one 256-byte
+// copy of the page's 16 k_scales and 16 v_scales.  The per-lane parts of the
+// addresses are constants kept in registers, so a copy costs one scalar
+// base per page and no vector arithmetic.
 template <int WPG>
 struct DmaPlan {
-  static constexpr int NJ = 16 / WPG;
-  uint32_t voff[NJ];
+  static constexpr int PPW = 4 / WPG;
+  uint32_t voff[4 * PPW];  // byte offset inside a page, LDS swizzle applied
+  const float* sptr;       // lane l: k_scale (l/16 even) or v_scale (odd) of key l%16 of page 0
 };
 template <int WPG>
-__device__ inline void make_plan(DmaPlan<WPG>& pl, int row_bytes, int kvh, int wave, int lane) {
+__device__ inline void make_plan(DmaPlan<WPG>& pl, const AttnArgs& a, int kvh, int wave, int lane) {
+  constexpr int PPW = DmaPlan<WPG>::PPW;
   const int q = lane >> 4, s = lane & 15;
+  const int row_bytes = a.n_kv_heads * kHeadDim;
 #pragma unroll
-  for (int j = 0; j < DmaPlan<WPG>::NJ; ++j) {
-    const int g = wave + WPG * j;
-    const int page = (WPG * j) >> 2;  // WPG divides 4, so this is g / 4
-    const int rr = 4 * (g & 3) + q;   // row inside the page
-    const int r = 16 * page + rr;     // row of the tile
-    pl.voff[j] = (uint32_t)(rr * row_bytes + kvh * kHeadDim + 16 * (s ^ swz(r)));
-  }
-}
-
-// Issue the copies of one step's four pages: K (and, for pass 2, V) row groups
-// shared over the waves, plus the 64 K and 64 V scales.
-template <int WPG, bool WITH_V>
-__device__ inline void issue_stage(Stage& st, const AttnArgs& a, const DmaPlan<WPG>& pl, long page_bytes, int kvh,
-                                   const Pages& pg, int wave, int lane) {
+  for (int i = 0; i < PPW; ++i) {
+    const int p = wave * PPW + i;
 #pragma unroll
-  for (int j = 0; j < DmaPlan<WPG>::NJ; ++j) {
-    const int page = (WPG * j) >> 2;
-    const int g = wave + WPG * j;
-    const long pbase = (long)pg.p[page] * page_bytes;
-    dma16(pl.voff[j], a.k_pool + pbase, lds_addr(st.k + kKeysPerGroup * kHeadDim * g));
-    if (WITH_V) dma16(pl.voff[j], a.v_pool + pbase, lds_addr(st.v + kKeysPerGroup * kHeadDim * g));
-  }
-  // k_scale by wave 0, v_scale by wave 1 (both by wave 0 when WPG == 1):
-  // lane l copies the scale of key l, page l/16
-  const int q = lane >> 4, s = lane & 15;
-  const int odd = -(q & 1), high = -((q >> 1) & 1);
-  const int lo = pg.p[0] ^ ((pg.p[0] ^ pg.p[1]) & odd);
-  const int hi = pg.p[2] ^ ((pg.p[2] ^ pg.p[3]) & odd);
-  const int ppage = lo ^ ((lo ^ hi) & high);
-  const long sidx = ((long)ppage * kPage + s) * a.n_kv_heads + kvh;
-  if (wave == 0) dma4(a.k_scale + sidx, lds_addr(&st.sc[0][0]));
-  if (wave == (WPG > 1 ? 1 : 0)) dma4(a.v_scale + sidx, lds_addr(&st.sc[1][0]));
-}
-
-// S^T of the step: for page p, lane l holds query row l%16 and keys
-// 4(l/16) + i of that page in register i.
-__device__ inline void qk_step(const int8_t* kb, const v4i (&qf)[4], int lane, v4i (&s)[4]) {
-  const int g = lane >> 4;
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const int r = 16 * p + (lane & 15);
-    v4i acc = {0, 0, 0, 0};
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int slot = (4 * c + g) ^ swz(r);
-      const v4i kf = *reinterpret_cast<const v4i*>(kb + r * kHeadDim + 16 * slot);
-      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(kf, qf[c], acc, 0, 0, 0);
+    for (int j = 0; j < 4; ++j) {
+      const int rr = 4 * j + q;  // key inside the page
+      pl.voff[4 * i + j] = (uint32_t)(rr * row_bytes + kvh * kHeadDim + 16 * (s ^ swz(16 * p + rr)));
     }
-    s[p] = acc;
+  }
+  pl.sptr = ((q & 1) ? a.v_scale : a.k_scale) + s * a.n_kv_heads + kvh;
+}
+
+template <int WPG, bool WITH_V, class S>
+__device__ inline void issue_stage(S& st, const AttnArgs& a, const DmaPlan<WPG>& pl, uint32_t page_bytes,
+                                   uint32_t scale_stride, const WavePages<WPG>& pg, int wave) {
+  constexpr int PPW = DmaPlan<WPG>::PPW;
+#pragma unroll
+  for (int i = 0; i < PPW; ++i) {
+    const int p = wave * PPW + i;
+    const uint32_t page = (uint32_t)pg.p[i];
+    const uint64_t off = (uint64_t)page * page_bytes;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      dma16(pl.voff[4 * i + j], a.k_pool + off, lds_addr(st.k + kKeysPerGroup * kHeadDim * (4 * p + j)));
+      if constexpr (WITH_V)
+        dma16(pl.voff[4 * i + j], a.v_pool + off, lds_addr(st.v + kKeysPerGroup * kHeadDim * (4 * p + j)));
+    }
+    dma4(pl.sptr + (uint64_t)page * scale_stride, lds_addr(&st.sc[p][0]));
   }
 }
 
 // Per-lane constants of one wave.
 struct RowCtx {
   int g;       // 16-lane row of the wave (0..3)
-  float rowf;  // q_scale * softmax_scale * log2(e) of this lane's query row
   int t_mask;  // causal bound of this lane's query row
 };
 
@@ -225,103 +219,169 @@ __device__ inline uint32_t key_mask(const TileBlocks& tb, int step, const RowCtx
   return m;
 }
 
-// Pass 1: running max of z = score*log2(e) + log2(v_scale) = (acc*k_scale)*rowf
-// + log2(v_scale).  Its row maximum Z makes P' = exp2(z - Z) <= 1 in pass 2,
-// so the row's largest P' is 1 and fixes the fixed-point scale.  Each lane
-// takes one log2 (key = lane) and the wave shares them through its own LDS
-// slice.
-template <bool MASKED>
-__device__ inline void pass1_step(const Stage& st, float* lvs_w, const v4i (&qf)[4], int lane, const RowCtx& rc,
-                                  uint32_t kmask, float& zmax) {
-  lvs_w[lane] = __builtin_amdgcn_logf(st.sc[1][lane]);
-  v4i s[4];
-  qk_step(st.k, qf, lane, s);
+// S^T = K . Q^T for HPW query heads and NP pages (p0 ..) of a step: K
+// fragment (16 keys x 64 channels, one ds_read_b128) feeds HPW products.
+// Afterwards s[h][pp] register i of lane l holds query row l%16 and key
+// 4(l/16) + i of page p0 + pp.
+template <int HPW, int NP>
+__device__ inline void qk_pages(const int8_t* kb, const v4i (&qf)[HPW][4], int p0, int lane, v4i (&s)[HPW][NP]) {
+  const int g = lane >> 4;
+#pragma unroll
+  for (int pp = 0; pp < NP; ++pp) {
+    const int r = 16 * (p0 + pp) + (lane & 15);
+#pragma unroll
+    for (int h = 0; h < HPW; ++h) s[h][pp] = v4i{0, 0, 0, 0};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int slot = (4 * c + g) ^ swz(r);
+      const v4i kf = *reinterpret_cast<const v4i*>(kb + r * kHeadDim + 16 * slot);
+#pragma unroll
+      for (int h = 0; h < HPW; ++h) s[h][pp] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kf, qf[h][c], s[h][pp], 0, 0, 0);
+    }
+  }
+}
+
+// The same with the fragment reads software-pipelined D fragments ahead of
+// their products.  The scheduling fences keep the compiler from sinking the
+// reads back next to their uses (it would otherwise reuse one register set
+// and wait out the full LDS latency before every product).
+template <int HPW, int NP, int D>
+__device__ inline void qk_pages_pipelined(const int8_t* kb, const v4i (&qf)[HPW][4], int p0, int lane,
+                                          v4i (&s)[HPW][NP]) {
+  constexpr int NF = 4 * NP;  // fragments: f = 4 * pp + c
+  const int g = lane >> 4;
+  auto read = [&](int f) {
+    const int r = 16 * (p0 + f / 4) + (lane & 15);
+    const int slot = (4 * (f % 4) + g) ^ swz(r);
+    return *reinterpret_cast<const v4i*>(kb + r * kHeadDim + 16 * slot);
+  };
+  v4i kf[NF];
+#pragma unroll
+  for (int f = 0; f < D; ++f) {
+    kf[f] = read(f);
+    __builtin_amdgcn_sched_barrier(0);  // issue in order: the first product waits for the first read only
+  }
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    if (f + D < NF) kf[f + D] = read(f + D);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int h = 0; h < HPW; ++h)
+      s[h][f / 4] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kf[f], qf[h][f % 4], f % 4 ? s[h][f / 4] : v4i{0, 0, 0, 0},
+                                                          0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Row-max launch, one step: running max of z = score*log2(e) + log2(v_scale)
+// = (acc*k_scale)*rowf + log2(v_scale) over the wave's NP pages for its HPW
+// heads.  Its row maximum Z makes P' = exp2(z - Z) <= 1 in pass 2, so the
+// row's largest P' is 1 and fixes the fixed-point scale.  Each lane takes one
+// log2 and the wave shares them through its own LDS slice.
+template <int HPW, int NP, bool MASKED, class S>
+__device__ inline void rowmax_step(const S& st, float* lvs_w, const v4i (&qf)[HPW][4], int p0, int lane, int g,
+                                   const float (&rowf)[HPW], uint32_t kmask, float (&zmax)[HPW]) {
+  lvs_w[lane] = __builtin_amdgcn_logf(st.sc[p0 + ((lane >> 4) & (NP - 1))][16 + (lane & 15)]);
+  v4i s[HPW][NP];
+  qk_pages<HPW, NP>(st.k, qf, p0, lane, s);
   __builtin_amdgcn_wave_barrier();
 #pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const float4 ks4 = *reinterpret_cast<const float4*>(&st.sc[0][16 * p + 4 * rc.g]);
-    const float4 lv4 = *reinterpret_cast<const float4*>(&lvs_w[16 * p + 4 * rc.g]);
-    float z[4];
+  for (int pp = 0; pp < NP; ++pp) {
+    const int p = p0 + pp;
+    const float4 ks4 = *reinterpret_cast<const float4*>(&st.sc[p][4 * g]);
+    const float4 lv4 = *reinterpret_cast<const float4*>(&lvs_w[16 * pp + 4 * g]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      z[i] = fmaf((float)s[p][i] * (&ks4.x)[i], rc.rowf, (&lv4.x)[i]);
-      if (MASKED) z[i] = ((kmask >> (4 * p + i)) & 1u) ? z[i] : -INFINITY;
+    for (int h = 0; h < HPW; ++h) {
+      float z[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        z[i] = fmaf((float)s[h][pp][i] * (&ks4.x)[i], rowf[h], (&lv4.x)[i]);
+        if (MASKED) z[i] = ((kmask >> (4 * p + i)) & 1u) ? z[i] : -INFINITY;
+      }
+      zmax[h] = fmaxf(fmaxf(zmax[h], fmaxf(z[0], z[1])), fmaxf(z[2], z[3]));
     }
-    zmax = fmaxf(fmaxf(zmax, fmaxf(z[0], z[1])), fmaxf(z[2], z[3]));
   }
   __builtin_amdgcn_wave_barrier();
 }
 
-// Pass 2: e = exp2(z - Z - log2 v_scale) = P, l += P, P' = P * v_scale <= 1,
-// per-page codes code = rint(P' * 127 / max P'), their weights ps * code as
-// the fixed-point integer x = rint(code * f), f = max P' * Xmax / (127 * cap),
-// split into two signed int8 digit planes x = d0 + 256 d1, then PV.
+// Page maxima over the four 16-lane rows for the four pages at once:
+// afterwards every lane holds all four.
+__device__ inline void page_maxima(float (&mx)[4]) {
+  float a = mx[0], b = mx[1], c = mx[2], d = mx[3];
+  swap16(a, b);
+  const float x01 = fmaxf(a, b);  // R0: p0(R0,R1)  R1: p1(R0,R1)  R2: p0(R2,R3)  R3: p1(R2,R3)
+  swap16(c, d);
+  const float x23 = fmaxf(c, d);
+  float e0 = x01, e1 = x23;
+  swap32(e0, e1);
+  const float y = fmaxf(e0, e1);  // row Rk holds the full max of page k
+  float g0 = y, g1 = y;
+  swap16(g0, g1);  // rows 0,1: (M0, M1); rows 2,3: (M2, M3)
+  float m0 = g0, m2 = g0, m1 = g1, m3 = g1;
+  swap32(m0, m2);  // every lane: m0 = M0, m2 = M2
+  swap32(m1, m3);
+  mx[0] = m0;
+  mx[1] = m1;
+  mx[2] = m2;
+  mx[3] = m3;
+}
+
+// Pass 2, one step for HPW heads: e = exp2(z - Z - log2 v_scale) = P, l += P,
+// P' = P * v_scale <= 1, per-page codes code = rint(P' * 127 / max P'), their
+// weights ps * code as the fixed-point integer x = rint(code * f),
+// f = max P' * Xmax / (127 * cap), split into two signed int8 digit planes
+// x = d0 + 256 d1, then PV.  Every K and V fragment read serves HPW heads.
 //
 // code * f is formed as (code * F + 2^15) >> 16 with F = rint(f * 2^16) < 2^24
 // by one 24-bit multiply-add; with a bias of 128 in the upper half, bytes 2
 // and 3 of the result are d0 + 128 and d1.
-template <bool MASKED>
-__device__ inline void pass2_step(const Stage& st, const v4i (&qf)[4], int lane, const RowCtx& rc, uint32_t kmask,
-                                  float neg_z, float& lsum, v4i (&acc)[2][16]) {
-  v4i s[4];
-  qk_step(st.k, qf, lane, s);
-  float pp[4][4];
-  float mx[4];
+template <int HPW, bool MASKED>
+__device__ inline void pass2_step(const Stage& st, const v4i (&qf)[HPW][4], int lane, int g, const float (&rowf)[HPW],
+                                  uint32_t kmask, const float (&neg_z)[HPW], float (&lsum)[HPW],
+                                  v4i (&acc)[HPW][2][16]) {
+  v4i s[HPW][4];
+  qk_pages_pipelined<HPW, 4, 8>(st.k, qf, 0, lane, s);
+  v4i dig[HPW][2];
 #pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const float4 ks4 = *reinterpret_cast<const float4*>(&st.sc[0][16 * p + 4 * rc.g]);
-    const float4 vs4 = *reinterpret_cast<const float4*>(&st.sc[1][16 * p + 4 * rc.g]);
+  for (int h = 0; h < HPW; ++h) {
+    float pp[4][4];
+    float mx[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float e = __builtin_amdgcn_exp2f(fmaf((float)s[p][i] * (&ks4.x)[i], rc.rowf, neg_z));
-      float pv = e * (&vs4.x)[i];
-      if (MASKED) {
-        const bool ok = (kmask >> (4 * p + i)) & 1u;
-        e = ok ? e : 0.f;
-        pv = ok ? pv : 0.f;
+    for (int p = 0; p < 4; ++p) {
+      const float4 ks4 = *reinterpret_cast<const float4*>(&st.sc[p][4 * g]);
+      const float4 vs4 = *reinterpret_cast<const float4*>(&st.sc[p][16 + 4 * g]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float e = __builtin_amdgcn_exp2f(fmaf((float)s[h][p][i] * (&ks4.x)[i], rowf[h], neg_z[h]));
+        float pv = e * (&vs4.x)[i];
+        if (MASKED) {
+          const bool ok = (kmask >> (4 * p + i)) & 1u;
+          e = ok ? e : 0.f;
+          pv = ok ? pv : 0.f;
+        }
+        lsum[h] += e;
+        pp[p][i] = pv;
       }
-      lsum += e;
-      pp[p][i] = pv;
+      mx[p] = fmaxf(fmaxf(pp[p][0], pp[p][1]), fmaxf(pp[p][2], pp[p][3]));
     }
-    mx[p] = fmaxf(fmaxf(pp[p][0], pp[p][1]), fmaxf(pp[p][2], pp[p][3]));
-  }
-  // page maxima over the four 16-lane rows: afterwards every lane holds all four
-  {
-    float a = mx[0], b = mx[1], c = mx[2], d = mx[3];
-    swap16(a, b);
-    const float x01 = fmaxf(a, b);  // R0: p0(R0,R1)  R1: p1(R0,R1)  R2: p0(R2,R3)  R3: p1(R2,R3)
-    swap16(c, d);
-    const float x23 = fmaxf(c, d);
-    float e0 = x01, e1 = x23;
-    swap32(e0, e1);
-    const float y = fmaxf(e0, e1);  // row Rk holds the full max of page k
-    float g0 = y, g1 = y;
-    swap16(g0, g1);  // rows 0,1: (M0, M1); rows 2,3: (M2, M3)
-    float m0 = g0, m2 = g0, m1 = g1, m3 = g1;
-    swap32(m0, m2);  // every lane: m0 = M0, m2 = M2
-    swap32(m1, m3);
-    mx[0] = m0;
-    mx[1] = m1;
-    mx[2] = m2;
-    mx[3] = m3;
-  }
-  v4i dig[2];
+    page_maxima(mx);
 #pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    // pages weighing below 2^-60 of the cap round to zero in this fixed point
-    const bool live = mx[p] > kTiny;
-    const float inv = live ? 127.0f * __builtin_amdgcn_rcpf(mx[p]) : 0.f;
-    const uint32_t F = (uint32_t)fmaf(mx[p], kFScale, 0.5f);
-    uint32_t r[4];
+    for (int p = 0; p < 4; ++p) {
+      // a page whose P' all lie below 2^-60 (masked ones are 0) gets F = 0 and
+      // finite codes, so its weights are exactly zero
+      const float inv = 127.0f * __builtin_amdgcn_rcpf(fmaxf(mx[p], kTiny));
+      const uint32_t F = (uint32_t)fmaf(mx[p], kFScale, 0.5f);
+      uint32_t r[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t code = __float_as_uint(fmaf(pp[p][i], inv, kTwo23));  // 2^23 + rint(P' * inv)
-      r[i] = __umul24(code, F) + kDigitBias;
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t code = __float_as_uint(fmaf(pp[p][i], inv, kTwo23));  // 2^23 + rint(P' * inv)
+        r[i] = __umul24(code, F) + kDigitBias;
+      }
+      const uint32_t w01 = __builtin_amdgcn_perm(r[1], r[0], 0x07060302u);
+      const uint32_t w23 = __builtin_amdgcn_perm(r[3], r[2], 0x07060302u);
+      dig[h][0][p] = (int)(__builtin_amdgcn_perm(w23, w01, 0x06040200u) ^ 0x80808080u);  // low digit, signed
+      dig[h][1][p] = (int)__builtin_amdgcn_perm(w23, w01, 0x07050301u);                 // high digit
     }
-    const uint32_t w01 = __builtin_amdgcn_perm(r[1], r[0], 0x07060302u);
-    const uint32_t w23 = __builtin_amdgcn_perm(r[3], r[2], 0x07060302u);
-    dig[0][p] = (int)(__builtin_amdgcn_perm(w23, w01, 0x06040200u) ^ 0x80808080u);  // low digit, signed
-    dig[1][p] = (int)__builtin_amdgcn_perm(w23, w01, 0x07050301u);                 // high digit
   }
 
   // V operand: lane (row g, column j) needs 16 keys of channel 16nt + j in the
@@ -329,161 +389,255 @@ __device__ inline void pass2_step(const Stage& st, const v4i (&qf)[4], int lane,
   // reads give slots 0-7 (pages 0, 1) and 8-15 (pages 2, 3).
   const int j = lane & 15;
   const int kk = j >> 1;
-  const int key1 = 16 * (kk >> 2) + 4 * rc.g + (kk & 3);
+  const int key1 = 16 * (kk >> 2) + 4 * g + (kk & 3);
   const int8_t* row1 = st.v + key1 * kHeadDim + 8 * (j & 1);
   const int8_t* row2 = row1 + 32 * kHeadDim;  // key1 + 32
   const int sw = swz(key1);
   const int sw2 = swz(key1 + 32);
-#pragma unroll
-  for (int nt = 0; nt < 16; ++nt) {
+  // reads run two column tiles ahead of their products (see qk_pages_pipelined)
+  constexpr int DV = 2;
+  auto read_v = [&](int nt) {
     const v2i lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32((WPA_LDS v2i*)(row1 + 16 * (nt ^ sw)));
     const v2i hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32((WPA_LDS v2i*)(row2 + 16 * (nt ^ sw2)));
-    const v4i vf = {lo.x, lo.y, hi.x, hi.y};
-    acc[0][nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(dig[0], vf, acc[0][nt], 0, 0, 0);
-    acc[1][nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(dig[1], vf, acc[1][nt], 0, 0, 0);
+    return v4i{lo.x, lo.y, hi.x, hi.y};
+  };
+  v4i vf[16];
+#pragma unroll
+  for (int nt = 0; nt < DV; ++nt) {
+    vf[nt] = read_v(nt);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int nt = 0; nt < 16; ++nt) {
+    if (nt + DV < 16) vf[nt + DV] = read_v(nt + DV);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int h = 0; h < HPW; ++h) {
+      acc[h][0][nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(dig[h][0], vf[nt], acc[h][0][nt], 0, 0, 0);
+      acc[h][1][nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(dig[h][1], vf[nt], acc[h][1][nt], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-template <int WPG, bool OUT_BF16>
-__global__ __launch_bounds__(64 * WPG, 2) void prefill_attn_kernel(AttnArgs a, const int32_t* __restrict__ pt_arg) {
-  __shared__ Stage st[2];
-  __shared__ alignas(16) float lvs[WPG][kStepKeys];  // per-wave log2(v_scale) of the step
-  const WPA_CONST int32_t* pt = (const WPA_CONST int32_t*)pt_arg;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-
-  int u = blockIdx.x;
-  const int hg = u % a.hgroups;
-  u /= a.hgroups;
-  const int kvh = u % a.n_kv_heads;
-  const int qt = a.n_tiles - 1 - u / a.n_kv_heads;  // longest tiles first
-
-  const int head = kvh * a.G + hg * WPG + wave;  // WPG divides G: every wave has a head
-  const int my_t = qt * kPage + (lane & 15);
-  const bool row_ok = my_t < a.n_tokens;
-
+// What a wave knows about its work item: workgroup u covers query tile qt,
+// KV head kvh and NW*HPW of its query heads; wave w takes heads
+// head0 .. head0+HPW-1 (16 query rows each).
+template <int NW, int HPW>
+struct Work {
+  int lane, wave, kvh, qt, head0, my_t;
+  bool row_ok;
   RowCtx rc;
-  rc.g = lane >> 4;
-  rc.t_mask = row_ok ? my_t : a.n_tokens - 1;
-
-  const TileBlocks tb = tile_blocks(qt, a.window_blocks, a.sink_blocks);
-  const int n_st = (tb.n_total + 3) >> 2;
-  const uint32_t kmask = key_mask(tb, n_st - 1, rc);
-
-  const int row_bytes = a.n_kv_heads * kHeadDim;
-  const long page_bytes = (long)kPage * row_bytes;
-  DmaPlan<WPG> plan;
-  make_plan<WPG>(plan, row_bytes, kvh, wave, lane);
-
-  // Start streaming the first pages before anything else.
-  const Pages pg0 = step_pages(pt, tb, 0);
-  issue_stage<WPG, false>(st[0], a, plan, page_bytes, kvh, pg0, wave, lane);
-
-  // Q codes of this lane's row in the B-operand layout (16 channels per chunk);
-  // rows past the end read the last token and are never stored.
-  v4i qf[4];
-  {
+  TileBlocks tb;
+  int n_st;  // steps of 64 keys
+  uint32_t kmask;
+  uint32_t page_bytes, scale_stride;
+  DmaPlan<NW> plan;
+  __device__ Work(const AttnArgs& a) {
+    lane = threadIdx.x & 63;
+    wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    int u = blockIdx.x;
+    const int hg = u % a.hgroups;
+    u /= a.hgroups;
+    kvh = u % a.n_kv_heads;
+    qt = a.n_tiles - 1 - u / a.n_kv_heads;  // longest tiles first
+    head0 = kvh * a.G + (hg * NW + wave) * HPW;
+    my_t = qt * kPage + (lane & 15);
+    row_ok = my_t < a.n_tokens;
+    rc.g = lane >> 4;
+    rc.t_mask = row_ok ? my_t : a.n_tokens - 1;
+    tb = tile_blocks(qt, a.window_blocks, a.sink_blocks);
+    n_st = (tb.n_total + 3) >> 2;
+    kmask = key_mask(tb, n_st - 1, rc);
+    page_bytes = (uint32_t)(kPage * a.n_kv_heads * kHeadDim);
+    scale_stride = (uint32_t)(kPage * a.n_kv_heads);
+    make_plan<NW>(plan, a, kvh, wave, lane);
+  }
+  // Q codes of this lane's row for heads hd0 .. in the B-operand layout (16
+  // channels per chunk) and rowf = q_scale * softmax_scale * log2(e); rows
+  // past the end read the last token and are never stored.
+  template <int H>
+  __device__ void load_q(const AttnArgs& a, int hd0, v4i (&qf)[H][4], float (&rowf)[H]) const {
     const int tq = row_ok ? my_t : a.n_tokens - 1;
-    const int8_t* qrow = a.q_i8 + ((long)tq * a.n_q_heads + head) * kHeadDim + 16 * rc.g;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) qf[c] = *reinterpret_cast<const v4i*>(qrow + 64 * c);
-    rc.rowf = row_ok ? a.q_scale[(long)tq * a.n_q_heads + head] * a.row_mul : 0.f;
+    for (int h = 0; h < H; ++h) {
+      const int8_t* qrow = a.q_i8 + ((long)tq * a.n_q_heads + hd0 + h) * kHeadDim + 16 * rc.g;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) qf[h][c] = *reinterpret_cast<const v4i*>(qrow + 64 * c);
+      rowf[h] = row_ok ? a.q_scale[(long)tq * a.n_q_heads + hd0 + h] * a.row_mul : 0.f;
+    }
   }
+  // First four bytes of the output row of (token t, head hd): the row-max
+  // launch leaves Z there and the attention launch overwrites it.
+  __device__ float* z_slot(const AttnArgs& a, int t, int hd, bool bf16) const {
+    const long e = ((long)t * a.n_q_heads + hd) * kHeadDim;
+    return bf16 ? reinterpret_cast<float*>(reinterpret_cast<uint16_t*>(a.out) + e)
+                : reinterpret_cast<float*>(a.out) + e;
+  }
+};
 
-  // The 2*n_st steps (pass 1, then pass 2 over the same page list) alternate
-  // between the two buffers.  A step waits for its own copies, syncs (every
-  // wave is then done with the other buffer), issues the next step's copies
-  // into the other buffer, then computes on its own.
-  const int n_all = 2 * n_st;
-  auto pages_of = [&](int step) { return step_pages(pt, tb, step < n_st ? step : step - n_st); };
-  Pages pg_next = pages_of(1 < n_all ? 1 : 0);
-  float* lvs_w = lvs[wave];
+// First launch, pass 1: the row maximum Z of z over the tile's key list for
+// every (query row, head).  It stages only K and the scales and needs few
+// registers, so four waves share each SIMD.  A wave takes HPW of the
+// workgroup's WPG query heads and 4/KS pages of each step (K fragments read
+// once serve HPW heads); the KS partial maxima of a row are combined through
+// LDS at the end.  A step waits for its own copies, syncs (every wave is then
+// done with the other buffer), issues the next step's copies into the other
+// buffer, then computes on its own.
+template <int WPG, bool OUT_BF16>
+__global__ __launch_bounds__(64 * WPG, 4) void row_max_kernel(AttnArgs a, const int32_t* __restrict__ pt_arg) {
+  constexpr int HPW = WPG >= 2 ? 2 : 1;  // query heads per wave
+  constexpr int NHP = WPG / HPW;          // head groups of the workgroup
+  constexpr int KS = WPG / NHP;           // key splits
+  constexpr int NP = 4 / KS;              // pages of a step per wave
+  __shared__ StageK st[2];
+  __shared__ alignas(16) float lvs[WPG][kStepKeys];  // per-wave log2(v_scale) of its pages
+  __shared__ float zpart[KS][WPG][16];
+  const WPA_CONST int32_t* pt = (const WPA_CONST int32_t*)pt_arg;
+  Work<WPG, 1> w(a);  // one wave per head for the copies; heads are regrouped below
+  issue_stage<WPG, false>(st[0], a, w.plan, w.page_bytes, w.scale_stride, wave_pages<WPG>(pt, w.tb, 0, w.wave), w.wave);
 
-  // ---- pass 1: row max of score*log2e + log2(v_scale)
-  float zmax = -INFINITY;
+  const int hp = w.wave % NHP, kh = w.wave / NHP;
+  const int head0 = w.head0 - w.wave + hp * HPW;  // first head of this wave
+  const int p0 = kh * NP;
+  v4i qf[HPW][4];
+  float rowf[HPW];
+  w.template load_q<HPW>(a, head0, qf, rowf);
+  wait_vmem();
+  WavePages<WPG> pg_next = wave_pages<WPG>(pt, w.tb, w.n_st > 1 ? 1 : 0, w.wave);
+  float* lvs_w = lvs[w.wave];
+
+  float zmax[HPW];
+#pragma unroll
+  for (int h = 0; h < HPW; ++h) zmax[h] = -INFINITY;
   int buf = 0;
-  for (int it = 0; it + 1 < n_st; ++it) {
+  for (int it = 0; it + 1 < w.n_st; ++it) {
     wait_stage();
     __syncthreads();
-    issue_stage<WPG, false>(st[buf ^ 1], a, plan, page_bytes, kvh, pg_next, wave, lane);
-    pg_next = pages_of(it + 2);
-    pass1_step<false>(st[buf], lvs_w, qf, lane, rc, 0u, zmax);
+    issue_stage<WPG, false>(st[buf ^ 1], a, w.plan, w.page_bytes, w.scale_stride, pg_next, w.wave);
+    if (it + 2 < w.n_st) pg_next = wave_pages<WPG>(pt, w.tb, it + 2, w.wave);
+    rowmax_step<HPW, NP, false>(st[buf], lvs_w, qf, p0, w.lane, w.rc.g, rowf, 0u, zmax);
     buf ^= 1;
   }
   wait_stage();
   __syncthreads();
-  issue_stage<WPG, true>(st[buf ^ 1], a, plan, page_bytes, kvh, pg_next, wave, lane);  // pass 2, first step
-  pg_next = pages_of(n_st + 1 < n_all ? n_st + 1 : n_st);
-  pass1_step<true>(st[buf], lvs_w, qf, lane, rc, kmask, zmax);
-  buf ^= 1;
-
-  const float neg_z = -rows_max(zmax);
-
-  // ---- pass 2
-  v4i acc[2][16];
+  rowmax_step<HPW, NP, true>(st[buf], lvs_w, qf, p0, w.lane, w.rc.g, rowf, w.kmask, zmax);
 #pragma unroll
-  for (int pl = 0; pl < 2; ++pl)
+  for (int h = 0; h < HPW; ++h) {
+    const float z = rows_max(zmax[h]);
+    if (w.rc.g == 0) zpart[kh][hp * HPW + h][w.lane] = z;
+  }
+  __syncthreads();
+  if (kh == 0 && w.rc.g == 0 && w.row_ok) {
 #pragma unroll
-    for (int nt = 0; nt < 16; ++nt) acc[pl][nt] = v4i{0, 0, 0, 0};
-  float lsum = 0.f;
-  for (int it = 0; it + 1 < n_st; ++it) {
+    for (int h = 0; h < HPW; ++h) {
+      float z = zpart[0][hp * HPW + h][w.lane];
+#pragma unroll
+      for (int k = 1; k < KS; ++k) z = fmaxf(z, zpart[k][hp * HPW + h][w.lane]);
+      *w.z_slot(a, w.my_t, head0 + h, OUT_BF16) = z;
+    }
+  }
+}
+
+// Second launch: pass 2 over the same key list with K and V staged, P codes,
+// digit planes and PV, then the epilogue.  HPW heads per wave: with HPW = 2 a
+// wave holds two heads' accumulators (256 registers) and runs alone on its
+// SIMD, every K and V fragment it reads feeding two heads; measured slower
+// than HPW = 1 at two waves per SIMD, which is what the launcher uses.
+template <int WPG, int HPW, bool OUT_BF16>
+__global__ __launch_bounds__(64 * (WPG / HPW), HPW == 2 ? 1 : 2) void prefill_attn_kernel(
+    AttnArgs a, const int32_t* __restrict__ pt_arg) {
+  constexpr int NW = WPG / HPW;
+  __shared__ Stage st[2];
+  const WPA_CONST int32_t* pt = (const WPA_CONST int32_t*)pt_arg;
+  Work<NW, HPW> w(a);
+  issue_stage<NW, true>(st[0], a, w.plan, w.page_bytes, w.scale_stride, wave_pages<NW>(pt, w.tb, 0, w.wave), w.wave);
+  v4i qf[HPW][4];
+  float rowf[HPW], neg_z[HPW], lsum[HPW];
+  w.template load_q<HPW>(a, w.head0, qf, rowf);
+  // rows past the end have rowf = 0 and any finite Z; their results stay in
+  // their own accumulator rows and are never stored
+#pragma unroll
+  for (int h = 0; h < HPW; ++h) {
+    neg_z[h] = w.row_ok ? -*w.z_slot(a, w.my_t, w.head0 + h, OUT_BF16) : 0.f;
+    lsum[h] = 0.f;
+  }
+  wait_vmem();
+  WavePages<NW> pg_next = wave_pages<NW>(pt, w.tb, w.n_st > 1 ? 1 : 0, w.wave);
+
+  v4i acc[HPW][2][16];
+#pragma unroll
+  for (int h = 0; h < HPW; ++h)
+#pragma unroll
+    for (int pl = 0; pl < 2; ++pl)
+#pragma unroll
+      for (int nt = 0; nt < 16; ++nt) acc[h][pl][nt] = v4i{0, 0, 0, 0};
+  int buf = 0;
+  for (int it = 0; it + 1 < w.n_st; ++it) {
     wait_stage();
     __syncthreads();
-    issue_stage<WPG, true>(st[buf ^ 1], a, plan, page_bytes, kvh, pg_next, wave, lane);
-    if (n_st + it + 2 < n_all) pg_next = pages_of(n_st + it + 2);
-    pass2_step<false>(st[buf], qf, lane, rc, 0u, neg_z, lsum, acc);
+    issue_stage<NW, true>(st[buf ^ 1], a, w.plan, w.page_bytes, w.scale_stride, pg_next, w.wave);
+    if (it + 2 < w.n_st) pg_next = wave_pages<NW>(pt, w.tb, it + 2, w.wave);
+    pass2_step<HPW, false>(st[buf], qf, w.lane, w.rc.g, rowf, 0u, neg_z, lsum, acc);
     buf ^= 1;
   }
   wait_stage();
   __syncthreads();
-  pass2_step<true>(st[buf], qf, lane, rc, kmask, neg_z, lsum, acc);
+  pass2_step<HPW, true>(st[buf], qf, w.lane, w.rc.g, rowf, w.kmask, neg_z, lsum, acc);
 
   // ---- epilogue: recombine the digit planes, scale by cap / (Xmax * l), store.
   // Output register i of tile nt is row 4g + i, channel 16nt + lane%16.
-  lsum = rows_sum(lsum);
-  const float rscale = kCap / (kXmax * lsum);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 4 * rc.g + i;
-    const float rr = __shfl(rscale, r);
-    const int t = qt * kPage + r;
-    if (t >= a.n_tokens) continue;
-    const long base = ((long)t * a.n_q_heads + head) * kHeadDim + (lane & 15);
+  for (int h = 0; h < HPW; ++h) {
+    const float rscale = kCap / (kXmax * rows_sum(lsum[h]));
 #pragma unroll
-    for (int nt = 0; nt < 16; ++nt) {
-      const float x = fmaf((float)acc[1][nt][i], 256.f, (float)acc[0][nt][i]);
-      const float o = x * rr;
-      if (OUT_BF16) {
-        const uint32_t u32 = __float_as_uint(o);  // round to nearest even
-        const uint16_t hb = (uint16_t)((u32 + 0x7fffu + ((u32 >> 16) & 1u)) >> 16);
-        reinterpret_cast<uint16_t*>(a.out)[base + 16 * nt] = hb;
-      } else {
-        reinterpret_cast<float*>(a.out)[base + 16 * nt] = o;
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * w.rc.g + i;
+      const float rr = __shfl(rscale, r);
+      const int t = w.qt * kPage + r;
+      if (t >= a.n_tokens) continue;
+      const long base = ((long)t * a.n_q_heads + w.head0 + h) * kHeadDim + (w.lane & 15);
+#pragma unroll
+      for (int nt = 0; nt < 16; ++nt) {
+        const float x = fmaf((float)acc[h][1][nt][i], 256.f, (float)acc[h][0][nt][i]);
+        const float o = x * rr;
+        if (OUT_BF16) {
+          const uint32_t u32 = __float_as_uint(o);  // round to nearest even
+          const uint16_t hb = (uint16_t)((u32 + 0x7fffu + ((u32 >> 16) & 1u)) >> 16);
+          reinterpret_cast<uint16_t*>(a.out)[base + 16 * nt] = hb;
+        } else {
+          reinterpret_cast<float*>(a.out)[base + 16 * nt] = o;
+        }
       }
     }
   }
 }
 
-template <int WPG>
+template <int WPG, int HPW, bool OUT_BF16>
+static void launch_wpg(const AttnArgs& a, unsigned grid, hipStream_t stream) {
+  hipLaunchKernelGGL((row_max_kernel<WPG, OUT_BF16>), dim3(grid), dim3(64 * WPG), 0, stream, a, a.page_table);
+  hipLaunchKernelGGL((prefill_attn_kernel<WPG, HPW, OUT_BF16>), dim3(grid), dim3(64 * (WPG / HPW)), 0, stream, a,
+                     a.page_table);
+}
+template <int WPG, int HPW>
 static void launch_wpg(const AttnArgs& a, bool out_bf16, unsigned grid, hipStream_t stream) {
-  if (out_bf16)
-    hipLaunchKernelGGL((prefill_attn_kernel<WPG, true>), dim3(grid), dim3(64 * WPG), 0, stream, a, a.page_table);
-  else
-    hipLaunchKernelGGL((prefill_attn_kernel<WPG, false>), dim3(grid), dim3(64 * WPG), 0, stream, a, a.page_table);
+  if (out_bf16) launch_wpg<WPG, HPW, true>(a, grid, stream);
+  else launch_wpg<WPG, HPW, false>(a, grid, stream);
 }
 
 hipError_t launch_prefill_attn(const AttnArgs& args_in, bool out_bf16, hipStream_t stream) {
   AttnArgs a = args_in;
   a.G = a.n_q_heads / a.n_kv_heads;
-  // waves (query heads) per workgroup: the largest of 4, 2, 1 dividing G
+  // query heads per workgroup: the largest of 4, 2, 1 dividing G; two heads
+  // per wave in pass 2 when that is even
   const int wpg = a.G % 4 == 0 ? 4 : (a.G % 2 == 0 ? 2 : 1);
   a.hgroups = a.G / wpg;
   a.n_tiles = (a.n_tokens + kPage - 1) / kPage;
   a.row_mul = a.softmax_scale * kLog2e;
   const unsigned grid = (unsigned)((long)a.n_tiles * a.n_kv_heads * a.hgroups);
-  if (wpg == 4) launch_wpg<4>(a, out_bf16, grid, stream);
-  else if (wpg == 2) launch_wpg<2>(a, out_bf16, grid, stream);
-  else launch_wpg<1>(a, out_bf16, grid, stream);
+  if (wpg == 4) launch_wpg<4, 1>(a, out_bf16, grid, stream);
+  else if (wpg == 2) launch_wpg<2, 1>(a, out_bf16, grid, stream);
+  else launch_wpg<1, 1>(a, out_bf16, grid, stream);
   return hipGetLastError();
 }
 
