@@ -305,21 +305,34 @@ __device__ inline void rowmax_step(const S& st, float* lvs_w, const v4i (&qf)[HP
 }
 
 // Page maxima over the four 16-lane rows for the four pages at once:
-// afterwards every lane holds all four.
-__device__ inline void page_maxima(float (&mx)[4]) {
-  float a = mx[0], b = mx[1], c = mx[2], d = mx[3];
-  swap16(a, b);
-  const float x01 = fmaxf(a, b);  // R0: p0(R0,R1)  R1: p1(R0,R1)  R2: p0(R2,R3)  R3: p1(R2,R3)
-  swap16(c, d);
-  const float x23 = fmaxf(c, d);
-  float e0 = x01, e1 = x23;
-  swap32(e0, e1);
-  const float y = fmaxf(e0, e1);  // row Rk holds the full max of page k
-  float g0 = y, g1 = y;
-  swap16(g0, g1);  // rows 0,1: (M0, M1); rows 2,3: (M2, M3)
-  float m0 = g0, m2 = g0, m1 = g1, m3 = g1;
-  swap32(m0, m2);  // every lane: m0 = M0, m2 = M2
-  swap32(m1, m3);
+// afterwards every lane holds all four.  The values are the bit patterns of
+// non-negative floats, whose unsigned order is their float order, so the
+// maxima are integer maxima (no NaN-quieting canonicalisations).
+__device__ inline uint32_t swap16u(uint32_t& a, uint32_t& b) {
+  auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+  a = r[0];
+  b = r[1];
+  return a;
+}
+__device__ inline void swap32u(uint32_t& a, uint32_t& b) {
+  auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+  a = r[0];
+  b = r[1];
+}
+__device__ inline void page_maxima(uint32_t (&mx)[4]) {
+  uint32_t a = mx[0], b = mx[1], c = mx[2], d = mx[3];
+  swap16u(a, b);
+  const uint32_t x01 = max(a, b);  // R0: p0(R0,R1)  R1: p1(R0,R1)  R2: p0(R2,R3)  R3: p1(R2,R3)
+  swap16u(c, d);
+  const uint32_t x23 = max(c, d);
+  uint32_t e0 = x01, e1 = x23;
+  swap32u(e0, e1);
+  const uint32_t y = max(e0, e1);  // row Rk holds the full max of page k
+  uint32_t g0 = y, g1 = y;
+  swap16u(g0, g1);  // rows 0,1: (M0, M1); rows 2,3: (M2, M3)
+  uint32_t m0 = g0, m2 = g0, m1 = g1, m3 = g1;
+  swap32u(m0, m2);  // every lane: m0 = M0, m2 = M2
+  swap32u(m1, m3);
   mx[0] = m0;
   mx[1] = m1;
   mx[2] = m2;
@@ -345,7 +358,7 @@ __device__ inline void pass2_step(const Stage& st, const v4i (&qf)[HPW][4], int 
 #pragma unroll
   for (int h = 0; h < HPW; ++h) {
     float pp[4][4];
-    float mx[4];
+    uint32_t mx[4];  // bit patterns of the page maxima of P' >= 0
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const float4 ks4 = *reinterpret_cast<const float4*>(&st.sc[p][4 * g]);
@@ -362,15 +375,16 @@ __device__ inline void pass2_step(const Stage& st, const v4i (&qf)[HPW][4], int 
         lsum[h] += e;
         pp[p][i] = pv;
       }
-      mx[p] = fmaxf(fmaxf(pp[p][0], pp[p][1]), fmaxf(pp[p][2], pp[p][3]));
+      mx[p] = max(max(__float_as_uint(pp[p][0]), __float_as_uint(pp[p][1])),
+                  max(__float_as_uint(pp[p][2]), __float_as_uint(pp[p][3])));
     }
     page_maxima(mx);
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       // a page whose P' all lie below 2^-60 (masked ones are 0) gets F = 0 and
       // finite codes, so its weights are exactly zero
-      const float inv = 127.0f * __builtin_amdgcn_rcpf(fmaxf(mx[p], kTiny));
-      const uint32_t F = (uint32_t)fmaf(mx[p], kFScale, 0.5f);
+      const float inv = 127.0f * __builtin_amdgcn_rcpf(__uint_as_float(max(mx[p], __float_as_uint(kTiny))));
+      const uint32_t F = (uint32_t)fmaf(__uint_as_float(mx[p]), kFScale, 0.5f);
       uint32_t r[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
