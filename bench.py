@@ -89,6 +89,61 @@ def cpu_baseline(case, seconds: float):
     }
 
 
+def bench_kv_write(args):
+    """The KV-pool writer on the 32k workload's shape: 32768 tokens x 4 KV heads of
+    bf16 K and V quantized into a 2048-page pool.  HBM-bound: the roofline is the
+    bytes it must move (bf16 rows in, int8 rows and float scales out, the slots)."""
+    import numpy as np
+    import torch
+    import windowed_int8_paged_amd as wpa
+    import workloads
+
+    n, hkv, pages = 32768, 4, 2048
+    kb, vb, _, _, slots, kp, vp, ks, vs = workloads.make_kv_rows(n, hkv, pages, seed=1003)
+    bf = lambda a: torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    k, v, sl = bf(kb), bf(vb), dev(slots)
+    kp, vp, ks, vs = dev(kp), dev(vp), dev(ks), dev(vs)
+    call = lambda: wpa.kv_write_i8(k, v, sl, kp, vp, ks, vs)
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        e0.record()
+        call()
+        e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+    nbytes = 2 * n * hkv * 256 * 2 + 4 * n + 2 * n * hkv * (256 + 4)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    res = {
+        "metric": "KV-pool write GB/s (bf16 K/V rows -> int8 pool pages + per-token scales)",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16->int8", "data": "synthetic",
+        "config": {"workload": f"KV-pool write, {n} tokens x {hkv} KV heads x 256 bf16 K and V into a "
+                               f"{pages}-page pool at shuffled slots", "bytes_per_call": nbytes},
+        "kernel_ms": {"kv_write_i8": round(ms, 4)},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "kv_write_i8"},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        m = 4096  # the oracle's writer on the first 4096 tokens of the same inputs
+        _, _, kf, vf, _, kp0, vp0, ks0, vs0 = workloads.make_kv_rows(n, hkv, pages, seed=1003)
+        t0 = time.perf_counter()
+        oracle.kv_write_i8(kf[:m], vf[:m], slots[:m], kp0, vp0, ks0, vs0)
+        dt = time.perf_counter() - t0
+        mbytes = 2 * m * hkv * 256 * 2 + 4 * m + 2 * m * hkv * (256 + 4)
+        res["cpu_baseline"] = {"value": round(mbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+                               "sample": f"oracle writer (numpy) on the first {m} of {n} tokens, {dt:.2f} s, "
+                                         f"bytes counted as for the GPU call (the oracle also copies the pool)"}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -98,6 +153,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--op", choices=["attention", "kv_write"], default="attention",
+                    help="attention: the headline step; kv_write: the KV-pool writer at the 32k shape")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -111,6 +168,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration(max(1, args.steps))
+        return
+    if args.op == "kv_write":
+        bench_kv_write(args)
         return
 
     import windowed_int8_paged_amd as wpa

@@ -129,6 +129,37 @@ wpa_status wpa_prefill_attn_i8(const int8_t* q_i8, const float* q_scale,
 wpa_status wpa_mask_counts(int n_tokens, int window_blocks, int sink_blocks, int32_t* counts,
                            hipStream_t stream);
 
+/*
+ * KV-pool writer: quantize new K and V rows and store them into the int8 pool
+ * at the given slots.  The pages describe the pool this path reads (int8
+ * tensor-core prefill attention page, "Why the attention, and why tensor
+ * cores": 16-token pages, rows token-major with stride n_kv_heads*256, one
+ * scale per token and KV head) but not how it is filled; each (token, KV head)
+ * row of K and of V is quantized with the per-row formula that page gives for
+ * Q ("one scale per row"), exactly as wpa_quantize_q_rows does:
+ *     amax = max |x|;  code = clamp(rint(x * (127 / amax)), -127, 127);
+ *     scale = amax / 127;   amax == 0 gives scale 0 and all-zero codes.
+ * Float32 arithmetic, IEEE division, round-half-to-even.
+ *
+ *   k, v          [n_tokens][n_kv_heads][256], dtype WPA_BF16 or WPA_F32,
+ *                 16-byte aligned (values that are not finite give
+ *                 unspecified codes).
+ *   slots         [n_tokens] int32, device: token t goes to pool slot
+ *                 slots[t] = physical page * 16 + position in the page.
+ *                 A slot outside [0, 16 * n_pool_pages) is skipped (nothing
+ *                 is written for that token); two tokens with the same slot
+ *                 race and either row may win.
+ *   k_pool, v_pool  [n_pool_pages][16][n_kv_heads][256] int8, 16-byte
+ *                 aligned; only the rows of the given slots are written.
+ *   k_scale, v_scale  [n_pool_pages][16][n_kv_heads] float32.
+ * Errors: NULL pointer -> WPA_ERR_NULL; n_tokens < 0, n_kv_heads <= 0 or
+ * n_pool_pages < 0 -> WPA_ERR_SHAPE; other dtype or misalignment ->
+ * WPA_ERR_UNSUPPORTED.
+ */
+wpa_status wpa_kv_write_i8(const void* k, const void* v, wpa_dtype dtype, int n_tokens, int n_kv_heads,
+                           const int32_t* slots, int n_pool_pages, int8_t* k_pool, int8_t* v_pool,
+                           float* k_scale, float* v_scale, hipStream_t stream);
+
 /* Static, human-readable name of a status ("WPA_OK", ...; "unknown status"). */
 const char* wpa_status_string(wpa_status s);
 

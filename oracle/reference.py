@@ -49,7 +49,7 @@ HEAD_DIM = 256
 PAGE = 16
 
 __all__ = [
-    "window_start_block", "attended_mask", "mask_counts", "quantize_q_rows",
+    "window_start_block", "attended_mask", "mask_counts", "quantize_q_rows", "kv_write_i8",
     "dequant_keys_values", "attention_exact", "attention_int8_mirror",
     "tile_rows", "HEAD_DIM", "PAGE",
 ]
@@ -114,6 +114,39 @@ def quantize_q_rows(q: np.ndarray):
     codes[~nz] = 0
     scale = np.where(nz, (amax / np.float32(127.0)).astype(np.float32), np.float32(0.0))
     return codes, scale.astype(np.float32)
+
+
+# ----------------------------------------------------------------------------
+# KV-pool writer: the pool the pages read, filled row by row  [465/Why]
+# ----------------------------------------------------------------------------
+
+def kv_write_i8(k: np.ndarray, v: np.ndarray, slots: np.ndarray, k_pool: np.ndarray,
+                v_pool: np.ndarray, k_scale: np.ndarray, v_scale: np.ndarray):
+    """Quantize K and V rows into copies of the int8 pool.
+
+    k, v: [n_tokens][n_kv_heads][256] (float32-representable values);
+    slots: [n_tokens] ints, slot = physical page * 16 + position in the page;
+    pools [P][16][Hkv][256] int8, scales [P][16][Hkv] float32.
+
+    The page gives the pool's layout (16-token pages, one scale per token and
+    KV head) but not how it is filled; each (token, head) row is quantized
+    with the per-row formula the page gives for Q (quantize_q_rows), and a
+    slot outside [0, 16 * P) is skipped.  Returns the four updated arrays.
+    """
+    k_pool, v_pool = k_pool.copy(), v_pool.copy()
+    k_scale, v_scale = k_scale.copy(), v_scale.copy()
+    n_pages = k_pool.shape[0]
+    kc, ks = quantize_q_rows(k)
+    vc, vs = quantize_q_rows(v)
+    for t, slot in enumerate(np.asarray(slots).tolist()):
+        if not 0 <= slot < n_pages * PAGE:
+            continue
+        page, pos = divmod(slot, PAGE)
+        k_pool[page, pos] = kc[t]
+        v_pool[page, pos] = vc[t]
+        k_scale[page, pos] = ks[t]
+        v_scale[page, pos] = vs[t]
+    return k_pool, v_pool, k_scale, v_scale
 
 
 # ----------------------------------------------------------------------------

@@ -29,14 +29,16 @@ def lib():
     L.wpa_prefill_attn_i8.argtypes = [vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, vp, ci, vp]
     L.wpa_quantize_q_rows.argtypes = [vp, ci, ci, ci, vp, vp, vp]
     L.wpa_mask_counts.argtypes = [ci, ci, ci, vp, vp]
+    L.wpa_kv_write_i8.argtypes = [vp, vp, ci, ci, ci, vp, ci, vp, vp, vp, vp, vp]
     L.wpa_status_string.argtypes = [ci]
     L.wpa_status_string.restype = ctypes.c_char_p
     return L
 
 
-def test_header_declares_the_three_entry_points():
+def test_header_declares_the_entry_points():
     fns = declared_functions()
-    for f in ("wpa_quantize_q_rows", "wpa_prefill_attn_i8", "wpa_mask_counts", "wpa_status_string"):
+    for f in ("wpa_quantize_q_rows", "wpa_prefill_attn_i8", "wpa_mask_counts", "wpa_kv_write_i8",
+              "wpa_status_string"):
         assert f in fns
 
 
@@ -113,6 +115,20 @@ def test_mask_counts_rejects_invalid_arguments(lib):
     assert m(10, 4, -1, P, None) == SHAPE
     assert m(10, 4, 1, None, None) == NULL
     assert m(0, 4, 1, None, None) == OK
+
+
+def test_kv_write_rejects_invalid_arguments(lib):
+    def w(k=P, v=P, dtype=1, n=4, hkv=2, slots=P, pages=1, kp=P, vp=P, ks=P, vs=P):
+        return lib.wpa_kv_write_i8(k, v, dtype, n, hkv, slots, pages, kp, vp, ks, vs, None)
+    assert w(n=-1) == SHAPE
+    assert w(hkv=0) == SHAPE
+    assert w(pages=-1) == SHAPE
+    assert w(dtype=3) == UNSUP
+    for name in ("k", "v", "slots", "kp", "vp", "ks", "vs"):
+        assert w(**{name: None}) == NULL, name
+    assert w(k=ctypes.c_void_p(0x100004)) == UNSUP
+    assert w(vp=ctypes.c_void_p(0x100008)) == UNSUP
+    assert w(n=0, k=None, v=None, slots=None, kp=None, vp=None, ks=None, vs=None) == OK
 
 
 def test_host_block_list_matches_oracle_counts():

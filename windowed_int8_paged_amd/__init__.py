@@ -10,6 +10,7 @@ Entry points mirror the C ABI in include/wpa.h:
                     window_blocks, sink_blocks, softmax_scale, out=None,
                     out_dtype=torch.bfloat16)          -> out
     mask_counts(n_tokens, window_blocks, sink_blocks, counts=None, device=None) -> counts
+    kv_write_i8(k, v, slots, k_pool, v_pool, k_scale, v_scale)  (writes the pools in place)
 """
 from __future__ import annotations
 
@@ -18,7 +19,7 @@ import os
 
 import torch
 
-__all__ = ["quantize_q_rows", "prefill_attn_i8", "mask_counts", "lib", "LIB_PATH",
+__all__ = ["quantize_q_rows", "prefill_attn_i8", "mask_counts", "kv_write_i8", "lib", "LIB_PATH",
            "HEAD_DIM", "PAGE_TOKENS", "WpaError"]
 
 HEAD_DIM = 256
@@ -43,6 +44,8 @@ def _load():
     L.wpa_prefill_attn_i8.restype = ci
     L.wpa_mask_counts.argtypes = [ci, ci, ci, vp, vp]
     L.wpa_mask_counts.restype = ci
+    L.wpa_kv_write_i8.argtypes = [vp, vp, ci, ci, ci, vp, ci, vp, vp, vp, vp, vp]
+    L.wpa_kv_write_i8.restype = ci
     L.wpa_status_string.argtypes = [ci]
     L.wpa_status_string.restype = ctypes.c_char_p
     return L
@@ -131,3 +134,26 @@ def mask_counts(n_tokens, window_blocks, sink_blocks, counts=None, device=None):
     _check(lib.wpa_mask_counts(int(n_tokens), int(window_blocks), int(sink_blocks), _ptr(counts),
                                _stream(counts.device)))
     return counts
+
+
+def kv_write_i8(k, v, slots, k_pool, v_pool, k_scale, v_scale):
+    """Quantize K and V rows ([n_tokens][n_kv_heads][256], bf16 or f32) into the
+    int8 pools at pool slots `slots` (int32 [n_tokens], page * 16 + position);
+    see include/wpa.h for the definition.  Writes the pools in place."""
+    if k.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("k must be bfloat16 or float32")
+    _dev(k, "k", k.dtype)
+    n, hkv, d = k.shape
+    if d != HEAD_DIM:
+        raise ValueError("head_dim must be 256")
+    _dev(v, "v", k.dtype, (n, hkv, d))
+    _dev(slots, "slots", torch.int32, (n,))
+    _dev(k_pool, "k_pool", torch.int8)
+    n_pool = k_pool.shape[0]
+    _dev(k_pool, "k_pool", torch.int8, (n_pool, PAGE_TOKENS, hkv, HEAD_DIM))
+    _dev(v_pool, "v_pool", torch.int8, (n_pool, PAGE_TOKENS, hkv, HEAD_DIM))
+    _dev(k_scale, "k_scale", torch.float32, (n_pool, PAGE_TOKENS, hkv))
+    _dev(v_scale, "v_scale", torch.float32, (n_pool, PAGE_TOKENS, hkv))
+    _check(lib.wpa_kv_write_i8(_ptr(k), _ptr(v), WPA_BF16 if k.dtype == torch.bfloat16 else WPA_F32, n, hkv,
+                               _ptr(slots), n_pool, _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale),
+                               _stream(k.device)))

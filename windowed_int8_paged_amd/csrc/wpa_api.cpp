@@ -51,6 +51,21 @@ wpa_status wpa_quantize_q_rows(const void* q, wpa_dtype q_dtype, int n_tokens, i
   return WPA_OK;
 }
 
+wpa_status wpa_kv_write_i8(const void* k, const void* v, wpa_dtype dtype, int n_tokens, int n_kv_heads,
+                           const int32_t* slots, int n_pool_pages, int8_t* k_pool, int8_t* v_pool, float* k_scale,
+                           float* v_scale, hipStream_t stream) {
+  if (n_tokens < 0 || n_kv_heads <= 0 || n_pool_pages < 0) return WPA_ERR_SHAPE;
+  if (dtype != WPA_BF16 && dtype != WPA_F32) return WPA_ERR_UNSUPPORTED;
+  if (n_tokens == 0) return WPA_OK;
+  if (!k || !v || !slots || !k_pool || !v_pool || !k_scale || !v_scale) return WPA_ERR_NULL;
+  if (!aligned16(k) || !aligned16(v) || !aligned16(k_pool) || !aligned16(v_pool)) return WPA_ERR_UNSUPPORTED;
+  if (2L * n_tokens * n_kv_heads * 32 > 0x7fffffffL * 256L) return WPA_ERR_UNSUPPORTED;
+  if (wpa::launch_kv_write(k, v, dtype == WPA_BF16, n_tokens, n_kv_heads, slots, n_pool_pages, k_pool, v_pool,
+                           k_scale, v_scale, stream) != hipSuccess)
+    return WPA_ERR_LAUNCH;
+  return WPA_OK;
+}
+
 wpa_status wpa_prefill_attn_i8(const int8_t* q_i8, const float* q_scale, const int8_t* k_pool,
                                const int8_t* v_pool, const float* k_scale, const float* v_scale,
                                const int32_t* page_table, int n_pool_pages, int n_tokens, int n_q_heads,

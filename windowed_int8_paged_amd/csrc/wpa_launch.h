@@ -25,6 +25,9 @@ struct AttnArgs {
 
 hipError_t launch_quantize_q_rows(const void* q, bool bf16, int n_tokens, int n_q_heads, int8_t* q_i8,
                                   float* q_scale, hipStream_t stream);
+hipError_t launch_kv_write(const void* k, const void* v, bool bf16, int n_tokens, int n_kv_heads,
+                           const int32_t* slots, int n_pool_pages, int8_t* k_pool, int8_t* v_pool, float* k_scale,
+                           float* v_scale, hipStream_t stream);
 hipError_t launch_mask_counts(int n_tokens, int window_blocks, int sink_blocks, int32_t* counts,
                               hipStream_t stream);
 hipError_t launch_prefill_attn(const AttnArgs& args, bool out_bf16, hipStream_t stream);

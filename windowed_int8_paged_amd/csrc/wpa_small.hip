@@ -1,4 +1,5 @@
-// Q row quantization and mask counts: the two small kernels of the path.
+// Q row quantization, the KV-pool writer and mask counts: the small kernels
+// of the path.
 //
 // Q quantization follows the int8 tensor-core prefill attention page, section
 // "Why the attention, and why tensor cores" (one scale per query row).  It is
@@ -12,18 +13,11 @@
 
 namespace wpa {
 
+// Eight consecutive channels of a 256-channel row held by one of 32 lanes.
 template <bool BF16>
-__global__ __launch_bounds__(256) void quantize_q_rows_kernel(const void* __restrict__ q,
-                                                              int8_t* __restrict__ q_i8,
-                                                              float* __restrict__ q_scale,
-                                                              long n_rows) {
-  const long row = ((long)blockIdx.x * blockDim.x + threadIdx.x) >> 5;
-  const int sub = threadIdx.x & 31;  // 8 channels each
-  if (row >= n_rows) return;         // whole half-waves drop out together
-
-  float v[8];
+__device__ inline void load8(const void* __restrict__ x, long row, int sub, float (&v)[8]) {
   if (BF16) {
-    const uint4 raw = reinterpret_cast<const uint4*>(q)[row * 32 + sub];
+    const uint4 raw = reinterpret_cast<const uint4*>(x)[row * 32 + sub];
     const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -31,19 +25,22 @@ __global__ __launch_bounds__(256) void quantize_q_rows_kernel(const void* __rest
       v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
     }
   } else {
-    const float4* p = reinterpret_cast<const float4*>(q) + row * 64 + sub * 2;
+    const float4* p = reinterpret_cast<const float4*>(x) + row * 64 + sub * 2;
     const float4 a = p[0], b = p[1];
     v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
     v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
   }
+}
 
+// Per-row quantization of a row spread over the 32 lanes of a half wave:
+// amax by a shuffle reduction, then IEEE division and round-half-to-even, as
+// the definition states.  Returns the lane's 8 codes and the row scale.
+__device__ inline uint2 quant8(const float (&v)[8], float& scale) {
   float amax = 0.f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
 #pragma unroll
   for (int off = 16; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 32));
-
-  // IEEE division and round-half-to-even, as the definition states.
   const float inv = amax > 0.f ? 127.0f / amax : 0.f;
   uint32_t lo = 0, hi = 0;
 #pragma unroll
@@ -54,8 +51,48 @@ __global__ __launch_bounds__(256) void quantize_q_rows_kernel(const void* __rest
     if (i < 4) lo |= b << (8 * i);
     else hi |= b << (8 * (i - 4));
   }
-  reinterpret_cast<uint2*>(q_i8)[row * 32 + sub] = make_uint2(lo, hi);
-  if (sub == 0) q_scale[row] = amax > 0.f ? amax / 127.0f : 0.f;
+  scale = amax > 0.f ? amax / 127.0f : 0.f;
+  return make_uint2(lo, hi);
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void quantize_q_rows_kernel(const void* __restrict__ q,
+                                                              int8_t* __restrict__ q_i8,
+                                                              float* __restrict__ q_scale,
+                                                              long n_rows) {
+  const long row = ((long)blockIdx.x * blockDim.x + threadIdx.x) >> 5;
+  const int sub = threadIdx.x & 31;  // 8 channels each
+  if (row >= n_rows) return;         // whole half-waves drop out together
+  float v[8], scale;
+  load8<BF16>(q, row, sub, v);
+  reinterpret_cast<uint2*>(q_i8)[row * 32 + sub] = quant8(v, scale);
+  if (sub == 0) q_scale[row] = scale;
+}
+
+// KV-pool writer: half wave r takes row r of K (r < n_rows) or row
+// r - n_rows of V, row = token * n_kv_heads + head, and stores its codes and
+// scale at the token's pool slot.  Slots outside the pool are skipped.
+template <bool BF16>
+__global__ __launch_bounds__(256) void kv_write_kernel(const void* __restrict__ k, const void* __restrict__ v,
+                                                       const int32_t* __restrict__ slots, int n_kv_heads,
+                                                       long n_rows, long n_slots, int8_t* __restrict__ k_pool,
+                                                       int8_t* __restrict__ v_pool, float* __restrict__ k_scale,
+                                                       float* __restrict__ v_scale) {
+  long r = ((long)blockIdx.x * blockDim.x + threadIdx.x) >> 5;
+  const int sub = threadIdx.x & 31;
+  if (r >= 2 * n_rows) return;
+  const bool is_v = r >= n_rows;
+  if (is_v) r -= n_rows;
+  const long token = r / n_kv_heads;
+  const int head = (int)(r - token * n_kv_heads);
+  const long slot = slots[token];
+  if (slot < 0 || slot >= n_slots) return;  // the whole half wave skips together
+  float x[8], scale;
+  load8<BF16>(is_v ? v : k, r, sub, x);
+  const uint2 codes = quant8(x, scale);
+  const long dst = slot * n_kv_heads + head;
+  reinterpret_cast<uint2*>(is_v ? v_pool : k_pool)[dst * 32 + sub] = codes;
+  if (sub == 0) (is_v ? v_scale : k_scale)[dst] = scale;
 }
 
 // counts[t] = number of keys row t attends: every listed block but the
@@ -78,6 +115,22 @@ hipError_t launch_quantize_q_rows(const void* q, bool bf16, int n_tokens, int n_
     hipLaunchKernelGGL(quantize_q_rows_kernel<true>, dim3(blocks), dim3(256), 0, stream, q, q_i8, q_scale, n_rows);
   else
     hipLaunchKernelGGL(quantize_q_rows_kernel<false>, dim3(blocks), dim3(256), 0, stream, q, q_i8, q_scale, n_rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_write(const void* k, const void* v, bool bf16, int n_tokens, int n_kv_heads,
+                           const int32_t* slots, int n_pool_pages, int8_t* k_pool, int8_t* v_pool, float* k_scale,
+                           float* v_scale, hipStream_t stream) {
+  const long n_rows = (long)n_tokens * n_kv_heads;
+  const long n_slots = (long)n_pool_pages * kPage;
+  const long threads = 2 * n_rows * 32;
+  const unsigned blocks = (unsigned)((threads + 255) / 256);
+  if (bf16)
+    hipLaunchKernelGGL(kv_write_kernel<true>, dim3(blocks), dim3(256), 0, stream, k, v, slots, n_kv_heads, n_rows,
+                       n_slots, k_pool, v_pool, k_scale, v_scale);
+  else
+    hipLaunchKernelGGL(kv_write_kernel<false>, dim3(blocks), dim3(256), 0, stream, k, v, slots, n_kv_heads, n_rows,
+                       n_slots, k_pool, v_pool, k_scale, v_scale);
   return hipGetLastError();
 }
 

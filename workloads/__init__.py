@@ -30,7 +30,7 @@ import numpy as np
 HEAD_DIM = 256
 PAGE = 16
 
-__all__ = ["Case", "CONFIGS", "make_config", "make_case", "HEAD_DIM", "PAGE"]
+__all__ = ["Case", "CONFIGS", "make_config", "make_case", "make_kv_rows", "HEAD_DIM", "PAGE"]
 
 
 @dataclasses.dataclass
@@ -179,3 +179,28 @@ def make_config(name: str, seed: int | None = None) -> Case:
     if seed is not None:
         kw["seed"] = seed
     return make_case(name=name, **kw)
+
+
+def make_kv_rows(n_tokens: int, n_kv_heads: int, n_pool_pages: int, seed: int):
+    """Seeded inputs of the KV-pool writer.
+
+    Returns (k_bf16, v_bf16, k_f32, v_f32, slots, k_pool, v_pool, k_scale, v_scale):
+    K and V rows drawn N(0, 1) and rounded to bf16 (bit patterns uint16, and
+    their exact float32 widening), [n_tokens][n_kv_heads][256]; slots, int32
+    [n_tokens], distinct pool slots in seeded random order; and a pool to write
+    into whose contents are random codes and scales, so untouched rows show.
+    Draw order: K, V, slots, pool codes, pool scales.
+    """
+    rng = np.random.default_rng(seed)
+    k = rng.standard_normal((n_tokens, n_kv_heads, HEAD_DIM), dtype=np.float32)
+    v = rng.standard_normal((n_tokens, n_kv_heads, HEAD_DIM), dtype=np.float32)
+    n_slots = n_pool_pages * PAGE
+    if n_tokens > n_slots:
+        raise ValueError("more tokens than pool slots")
+    slots = rng.permutation(n_slots)[:n_tokens].astype(np.int32)
+    k_pool = rng.integers(-127, 128, size=(n_pool_pages, PAGE, n_kv_heads, HEAD_DIM), dtype=np.int8)
+    v_pool = rng.integers(-127, 128, size=(n_pool_pages, PAGE, n_kv_heads, HEAD_DIM), dtype=np.int8)
+    k_scale = rng.uniform(0.005, 0.02, size=(n_pool_pages, PAGE, n_kv_heads)).astype(np.float32)
+    v_scale = rng.uniform(0.005, 0.02, size=(n_pool_pages, PAGE, n_kv_heads)).astype(np.float32)
+    kb, vb = _round_to_bf16_bits(k), _round_to_bf16_bits(v)
+    return (kb, vb, _bf16_bits_to_f32(kb), _bf16_bits_to_f32(vb), slots, k_pool, v_pool, k_scale, v_scale)
