@@ -56,15 +56,20 @@ def copy_calibration(steps: int) -> None:
     print(json.dumps({"copy_calibration_bytes_per_direction": n, "launches": steps}), flush=True)
 
 
+def blas_threads() -> int:
+    """Threads the oracle's numpy BLAS calls run on."""
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        return 1
+
+
 def cpu_baseline(case, seconds: float):
     """Time the oracle's int8 mirror (as it stands) on a bounded sample of tiles."""
     import numpy as np
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
+    threads = blas_threads()
     n_tiles = (case.n_tokens + 15) // 16
     # tiles past the window's fill-up (full-length key lists), else the later half,
     # visited with a stride of 7 so the sample spreads over the sequence
@@ -144,6 +149,80 @@ def bench_kv_write(args):
     print(json.dumps(res), flush=True)
 
 
+def bench_chunk(args):
+    """Chunked prefill past the pages' 64k batched limit: the query rows
+    65536 .. 69631 (16 q heads / 4 KV heads, window 256 blocks + 1 sink block)
+    over a cache of 69632 tokens already in the pool; quantize + attention."""
+    import numpy as np
+    import torch
+    import windowed_int8_paged_amd as wpa
+    import workloads
+
+    q_start, n = 65536, 4096
+    case = workloads.make_case(name="chunk", n_tokens=q_start + n, n_q_heads=16, n_kv_heads=4, window_blocks=256,
+                               sink_blocks=1, seed=1006)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    q = torch.from_numpy(case.q_bf16[q_start:].view(np.int16)).cuda().view(torch.bfloat16)
+    kp, vp, ks, vs, pt = (dev(a) for a in (case.k_pool, case.v_pool, case.k_scale, case.v_scale, case.page_table))
+    q_i8 = torch.empty((n, 16, 256), dtype=torch.int8, device="cuda")
+    q_scale = torch.empty((n, 16), dtype=torch.float32, device="cuda")
+    out = torch.empty((n, 16, 256), dtype=torch.bfloat16, device="cuda")
+    counts = wpa.mask_counts_chunk(q_start, n, 256, 1)
+    torch.cuda.synchronize()
+    keys = int(counts.to(torch.int64).sum().item())
+    ops = 4.0 * keys * 256 * 16
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        wpa.quantize_q_rows(q, q_i8, q_scale)
+        if ev is not None:
+            ev[1].record()
+        wpa.prefill_attn_i8_chunk(q_start, q_i8, q_scale, kp, vp, ks, vs, pt, 256, 1, case.softmax_scale, out=out)
+        if ev is not None:
+            ev[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    attn_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    quant_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    ms = wall * 1e3 / args.steps
+    res = {
+        "metric": "int8 TOPS, hd256 windowed prefill attn, 4096-row chunk at position 65536",
+        "value": round(ops / (ms * 1e-3) / 1e12, 2), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int8", "data": "synthetic",
+        "config": {"workload": "chunked prefill: query rows 65536..69631 of a 69632-token sequence, 16 q heads / "
+                               "4 kv heads, window 256 blocks + 1 sink block, int8 paged pool of 4352 shuffled "
+                               "16-token pages, bf16 Q and output", "attended_keys": keys, "int8_ops_per_step": ops},
+        "kernel_ms": {"quantize_q_rows": round(quant_ms, 4), "prefill_attn_i8_chunk": round(attn_ms, 4)},
+        "roofline": {"bound": "mfma", "achieved": round(ops / (attn_ms * 1e-3) / 1e12, 2), "peak": PEAK_INT8_TOPS,
+                     "unit": "TFLOP/s", "frac": round(ops / (attn_ms * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4),
+                     "traffic": None, "kernel": "prefill_attn_i8_chunk"},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        tiles, t1 = [], time.perf_counter()
+        for tile in range(q_start // 16, (q_start + n) // 16, 37):
+            oracle.attention_int8_mirror(case, tiles=[tile])
+            tiles.append(tile)
+            if time.perf_counter() - t1 >= args.cpu_seconds:
+                break
+        dt = time.perf_counter() - t1
+        rows = np.concatenate([oracle.tile_rows(case.n_tokens, t) for t in tiles])
+        cops = 4.0 * oracle.mask_counts(case.n_tokens, 256, 1)[rows].sum() * 256 * 16
+        res["cpu_baseline"] = {"value": cops / dt / 1e12, "unit": "TOPS", "cores": blas_threads(), "kind": "oracle",
+                               "sample": f"int8-mirror oracle on {len(tiles)} of {n // 16} chunk tiles, {dt:.1f} s"}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -153,8 +232,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true")
-    ap.add_argument("--op", choices=["attention", "kv_write"], default="attention",
-                    help="attention: the headline step; kv_write: the KV-pool writer at the 32k shape")
+    ap.add_argument("--op", choices=["attention", "kv_write", "chunk"], default="attention",
+                    help="attention: the headline step; kv_write: the KV-pool writer at the 32k shape; "
+                         "chunk: a 4096-row prefill chunk at position 65536 over a 69632-token cache")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -171,6 +251,9 @@ def main():
         return
     if args.op == "kv_write":
         bench_kv_write(args)
+        return
+    if args.op == "chunk":
+        bench_chunk(args)
         return
 
     import windowed_int8_paged_amd as wpa

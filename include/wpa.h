@@ -119,6 +119,29 @@ wpa_status wpa_prefill_attn_i8(const int8_t* q_i8, const float* q_scale,
                                void* out, wpa_dtype out_dtype, hipStream_t stream);
 
 /*
+ * Chunked prefill: the same attention for the query rows at sequence positions
+ * q_start .. q_start + n_tokens - 1 over a pool that already holds the keys
+ * 0 .. q_start + n_tokens - 1 (the rows before the chunk came from earlier
+ * calls).  Row i of q_i8, q_scale and out is position q_start + i; its
+ * attended set is A(q_start + i) as defined above, so splitting a prefill
+ * into chunks gives bitwise the same rows as one call.  q_start must be a
+ * multiple of 16 (the chunk starts on a page, keeping the window start fixed
+ * per 16-row tile).  page_table covers ceil((q_start + n_tokens)/16) blocks
+ * and n_pool_pages must be at least that.  Other arguments, layouts and
+ * errors as wpa_prefill_attn_i8; in addition q_start < 0 -> WPA_ERR_SHAPE and
+ * q_start % 16 != 0 -> WPA_ERR_UNSUPPORTED.  (The pages' batched prefill
+ * stops at 64k context and hands longer prompts to the token path; int8
+ * tensor-core prefill attention page, "Proof of speedup".)
+ */
+wpa_status wpa_prefill_attn_i8_chunk(const int8_t* q_i8, const float* q_scale,
+                                     const int8_t* k_pool, const int8_t* v_pool,
+                                     const float* k_scale, const float* v_scale,
+                                     const int32_t* page_table, int n_pool_pages,
+                                     int q_start, int n_tokens, int n_q_heads, int n_kv_heads,
+                                     int window_blocks, int sink_blocks, float softmax_scale,
+                                     void* out, wpa_dtype out_dtype, hipStream_t stream);
+
+/*
  * counts[t] = |A(t)| for t in [0, n_tokens), computed by walking the same key
  * block list the attention kernel walks (the mask of the int8 tensor-core
  * prefill attention page, "Why the attention, and why tensor cores": window
@@ -128,6 +151,12 @@ wpa_status wpa_prefill_attn_i8(const int8_t* q_i8, const float* q_scale,
  */
 wpa_status wpa_mask_counts(int n_tokens, int window_blocks, int sink_blocks, int32_t* counts,
                            hipStream_t stream);
+
+/* counts[i] = |A(q_start + i)| for i in [0, n_tokens): the counts of a chunk
+ * (wpa_prefill_attn_i8_chunk).  Errors as wpa_mask_counts, plus q_start < 0
+ * -> WPA_ERR_SHAPE. */
+wpa_status wpa_mask_counts_chunk(int q_start, int n_tokens, int window_blocks, int sink_blocks,
+                                 int32_t* counts, hipStream_t stream);
 
 /*
  * KV-pool writer: quantize new K and V rows and store them into the int8 pool

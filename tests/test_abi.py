@@ -30,6 +30,8 @@ def lib():
     L.wpa_quantize_q_rows.argtypes = [vp, ci, ci, ci, vp, vp, vp]
     L.wpa_mask_counts.argtypes = [ci, ci, ci, vp, vp]
     L.wpa_kv_write_i8.argtypes = [vp, vp, ci, ci, ci, vp, ci, vp, vp, vp, vp, vp]
+    L.wpa_prefill_attn_i8_chunk.argtypes = [vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, cf, vp, ci, vp]
+    L.wpa_mask_counts_chunk.argtypes = [ci, ci, ci, ci, vp, vp]
     L.wpa_status_string.argtypes = [ci]
     L.wpa_status_string.restype = ctypes.c_char_p
     return L
@@ -38,7 +40,7 @@ def lib():
 def test_header_declares_the_entry_points():
     fns = declared_functions()
     for f in ("wpa_quantize_q_rows", "wpa_prefill_attn_i8", "wpa_mask_counts", "wpa_kv_write_i8",
-              "wpa_status_string"):
+              "wpa_prefill_attn_i8_chunk", "wpa_mask_counts_chunk", "wpa_status_string"):
         assert f in fns
 
 
@@ -129,6 +131,25 @@ def test_kv_write_rejects_invalid_arguments(lib):
     assert w(k=ctypes.c_void_p(0x100004)) == UNSUP
     assert w(vp=ctypes.c_void_p(0x100008)) == UNSUP
     assert w(n=0, k=None, v=None, slots=None, kp=None, vp=None, ks=None, vs=None) == OK
+
+
+def test_chunk_entry_points_reject_invalid_arguments(lib):
+    def c(q_start=32, n=64, n_pool=6, **kw):
+        args = dict(q=P, qs=P, k=P, v=P, ks=P, vs=P, pt=P, hq=4, hkv=2, W=0, S=0, scale=0.0625, out=P, dtype=1)
+        args.update(kw)
+        return lib.wpa_prefill_attn_i8_chunk(args["q"], args["qs"], args["k"], args["v"], args["ks"], args["vs"],
+                                             args["pt"], n_pool, q_start, n, args["hq"], args["hkv"], args["W"],
+                                             args["S"], args["scale"], args["out"], args["dtype"], None)
+    assert c(q_start=-16) == SHAPE
+    assert c(n_pool=5) == SHAPE            # keys 0..95 need 6 pages
+    assert c(q_start=8) == UNSUP           # the chunk must start on a page
+    assert c(q=None) == NULL
+    assert c(n=0, q=None, out=None) == OK
+    m = lib.wpa_mask_counts_chunk
+    assert m(-16, 10, 4, 1, P, None) == SHAPE
+    assert m(16, -1, 4, 1, P, None) == SHAPE
+    assert m(16, 10, 4, 1, None, None) == NULL
+    assert m(16, 0, 4, 1, None, None) == OK
 
 
 def test_host_block_list_matches_oracle_counts():

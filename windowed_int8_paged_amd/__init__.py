@@ -11,6 +11,8 @@ Entry points mirror the C ABI in include/wpa.h:
                     out_dtype=torch.bfloat16)          -> out
     mask_counts(n_tokens, window_blocks, sink_blocks, counts=None, device=None) -> counts
     kv_write_i8(k, v, slots, k_pool, v_pool, k_scale, v_scale)  (writes the pools in place)
+    prefill_attn_i8_chunk(q_start, q_i8, q_scale, ...same as prefill_attn_i8...) -> out
+    mask_counts_chunk(q_start, n_tokens, window_blocks, sink_blocks, counts=None, device=None) -> counts
 """
 from __future__ import annotations
 
@@ -19,7 +21,8 @@ import os
 
 import torch
 
-__all__ = ["quantize_q_rows", "prefill_attn_i8", "mask_counts", "kv_write_i8", "lib", "LIB_PATH",
+__all__ = ["quantize_q_rows", "prefill_attn_i8", "prefill_attn_i8_chunk", "mask_counts", "mask_counts_chunk",
+           "kv_write_i8", "lib", "LIB_PATH",
            "HEAD_DIM", "PAGE_TOKENS", "WpaError"]
 
 HEAD_DIM = 256
@@ -44,6 +47,10 @@ def _load():
     L.wpa_prefill_attn_i8.restype = ci
     L.wpa_mask_counts.argtypes = [ci, ci, ci, vp, vp]
     L.wpa_mask_counts.restype = ci
+    L.wpa_prefill_attn_i8_chunk.argtypes = [vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, cf, vp, ci, vp]
+    L.wpa_prefill_attn_i8_chunk.restype = ci
+    L.wpa_mask_counts_chunk.argtypes = [ci, ci, ci, ci, vp, vp]
+    L.wpa_mask_counts_chunk.restype = ci
     L.wpa_kv_write_i8.argtypes = [vp, vp, ci, ci, ci, vp, ci, vp, vp, vp, vp, vp]
     L.wpa_kv_write_i8.restype = ci
     L.wpa_status_string.argtypes = [ci]
@@ -101,6 +108,20 @@ def quantize_q_rows(q, q_i8=None, q_scale=None):
 def prefill_attn_i8(q_i8, q_scale, k_pool, v_pool, k_scale, v_scale, page_table,
                     window_blocks, sink_blocks, softmax_scale, out=None, out_dtype=torch.bfloat16):
     """Paged int8 prefill attention; see include/wpa.h for the definition."""
+    return _prefill(None, q_i8, q_scale, k_pool, v_pool, k_scale, v_scale, page_table,
+                    window_blocks, sink_blocks, softmax_scale, out, out_dtype)
+
+
+def prefill_attn_i8_chunk(q_start, q_i8, q_scale, k_pool, v_pool, k_scale, v_scale, page_table,
+                          window_blocks, sink_blocks, softmax_scale, out=None, out_dtype=torch.bfloat16):
+    """The query rows at positions q_start .. q_start+n-1 (q_start a multiple of 16)
+    over a pool holding keys 0 .. q_start+n-1; see include/wpa.h."""
+    return _prefill(int(q_start), q_i8, q_scale, k_pool, v_pool, k_scale, v_scale, page_table,
+                    window_blocks, sink_blocks, softmax_scale, out, out_dtype)
+
+
+def _prefill(q_start, q_i8, q_scale, k_pool, v_pool, k_scale, v_scale, page_table,
+             window_blocks, sink_blocks, softmax_scale, out, out_dtype):
     _dev(q_i8, "q_i8", torch.int8)
     n, hq, d = q_i8.shape
     _dev(q_scale, "q_scale", torch.float32, (n, hq))
@@ -112,18 +133,21 @@ def prefill_attn_i8(q_i8, q_scale, k_pool, v_pool, k_scale, v_scale, page_table,
     _dev(k_scale, "k_scale", torch.float32, (n_pool, page, hkv))
     _dev(v_scale, "v_scale", torch.float32, (n_pool, page, hkv))
     _dev(page_table, "page_table", torch.int32)
-    if page_table.numel() < (n + PAGE_TOKENS - 1) // PAGE_TOKENS:
-        raise ValueError("page_table is shorter than ceil(n_tokens/16)")
+    if page_table.numel() < ((q_start or 0) + n + PAGE_TOKENS - 1) // PAGE_TOKENS:
+        raise ValueError("page_table is shorter than ceil((q_start + n_tokens)/16)")
     if out is None:
         out = torch.empty((n, hq, d), dtype=out_dtype, device=q_i8.device)
     if out.dtype not in (torch.bfloat16, torch.float32):
         raise TypeError("out must be bfloat16 or float32")
     _dev(out, "out", out.dtype, (n, hq, d))
-    _check(lib.wpa_prefill_attn_i8(
-        _ptr(q_i8), _ptr(q_scale), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale),
-        _ptr(page_table), n_pool, n, hq, hkv, int(window_blocks), int(sink_blocks),
-        float(softmax_scale), _ptr(out), WPA_BF16 if out.dtype == torch.bfloat16 else WPA_F32,
-        _stream(q_i8.device)))
+    common = (_ptr(q_i8), _ptr(q_scale), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale),
+              _ptr(page_table), n_pool)
+    tail = (n, hq, hkv, int(window_blocks), int(sink_blocks), float(softmax_scale), _ptr(out),
+            WPA_BF16 if out.dtype == torch.bfloat16 else WPA_F32, _stream(q_i8.device))
+    if q_start is None:
+        _check(lib.wpa_prefill_attn_i8(*common, *tail))
+    else:
+        _check(lib.wpa_prefill_attn_i8_chunk(*common, q_start, *tail))
     return out
 
 
@@ -133,6 +157,15 @@ def mask_counts(n_tokens, window_blocks, sink_blocks, counts=None, device=None):
     _dev(counts, "counts", torch.int32, (n_tokens,))
     _check(lib.wpa_mask_counts(int(n_tokens), int(window_blocks), int(sink_blocks), _ptr(counts),
                                _stream(counts.device)))
+    return counts
+
+
+def mask_counts_chunk(q_start, n_tokens, window_blocks, sink_blocks, counts=None, device=None):
+    if counts is None:
+        counts = torch.empty((n_tokens,), dtype=torch.int32, device=device or "cuda")
+    _dev(counts, "counts", torch.int32, (n_tokens,))
+    _check(lib.wpa_mask_counts_chunk(int(q_start), int(n_tokens), int(window_blocks), int(sink_blocks),
+                                     _ptr(counts), _stream(counts.device)))
     return counts
 
 

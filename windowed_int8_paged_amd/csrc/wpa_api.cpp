@@ -16,7 +16,7 @@ long ceil_div(long a, long b) { return (a + b - 1) / b; }
 
 // Largest number of keys any row attends: full causal -> n_tokens; otherwise
 // the last 'window_blocks' blocks plus the sink blocks, capped by n_tokens.
-long max_keys_per_row(int n_tokens, int window_blocks, int sink_blocks) {
+long max_keys_per_row(long n_tokens, int window_blocks, int sink_blocks) {
   if (window_blocks <= 0) return n_tokens;
   const long w = (long)WPA_PAGE_TOKENS * ((long)window_blocks + (long)sink_blocks);
   return w < n_tokens ? w : n_tokens;
@@ -66,20 +66,26 @@ wpa_status wpa_kv_write_i8(const void* k, const void* v, wpa_dtype dtype, int n_
   return WPA_OK;
 }
 
-wpa_status wpa_prefill_attn_i8(const int8_t* q_i8, const float* q_scale, const int8_t* k_pool,
-                               const int8_t* v_pool, const float* k_scale, const float* v_scale,
-                               const int32_t* page_table, int n_pool_pages, int n_tokens, int n_q_heads,
-                               int n_kv_heads, int window_blocks, int sink_blocks, float softmax_scale,
-                               void* out, wpa_dtype out_dtype, hipStream_t stream) {
-  if (n_tokens < 0 || n_q_heads <= 0 || n_kv_heads <= 0 || n_q_heads % n_kv_heads != 0) return WPA_ERR_SHAPE;
+}  // extern "C"
+
+namespace {
+
+wpa_status prefill_attn(const int8_t* q_i8, const float* q_scale, const int8_t* k_pool, const int8_t* v_pool,
+                        const float* k_scale, const float* v_scale, const int32_t* page_table, int n_pool_pages,
+                        int q_start, int n_tokens, int n_q_heads, int n_kv_heads, int window_blocks,
+                        int sink_blocks, float softmax_scale, void* out, wpa_dtype out_dtype, hipStream_t stream) {
+  if (n_tokens < 0 || q_start < 0 || n_q_heads <= 0 || n_kv_heads <= 0 || n_q_heads % n_kv_heads != 0)
+    return WPA_ERR_SHAPE;
   if (sink_blocks < 0 || !std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return WPA_ERR_SHAPE;
-  if (n_pool_pages < ceil_div(n_tokens, WPA_PAGE_TOKENS) || n_pool_pages < 0) return WPA_ERR_SHAPE;
+  const long seq = (long)q_start + n_tokens;  // keys 0 .. seq-1 are in the pool
+  if (n_pool_pages < 0 || n_pool_pages < ceil_div(seq, WPA_PAGE_TOKENS)) return WPA_ERR_SHAPE;
   if (out_dtype != WPA_BF16 && out_dtype != WPA_F32) return WPA_ERR_UNSUPPORTED;
+  if (q_start % WPA_PAGE_TOKENS != 0 || seq > 0x7fffffffL - WPA_PAGE_TOKENS) return WPA_ERR_UNSUPPORTED;
   if (n_tokens == 0) return WPA_OK;
   if (!q_i8 || !q_scale || !k_pool || !v_pool || !k_scale || !v_scale || !page_table || !out)
     return WPA_ERR_NULL;
   if (!aligned16(q_i8) || !aligned16(k_pool) || !aligned16(v_pool)) return WPA_ERR_UNSUPPORTED;
-  if (max_keys_per_row(n_tokens, window_blocks, sink_blocks) > WPA_MAX_KEYS_PER_ROW) return WPA_ERR_UNSUPPORTED;
+  if (max_keys_per_row(seq, window_blocks, sink_blocks) > WPA_MAX_KEYS_PER_ROW) return WPA_ERR_UNSUPPORTED;
   const long n_tiles = ceil_div(n_tokens, WPA_PAGE_TOKENS);
   if (n_tiles * n_kv_heads * ((n_q_heads / n_kv_heads + 1) / 2) > 0x7fffffffL) return WPA_ERR_UNSUPPORTED;
 
@@ -98,18 +104,53 @@ wpa_status wpa_prefill_attn_i8(const int8_t* q_i8, const float* q_scale, const i
   a.window_blocks = window_blocks;
   a.sink_blocks = sink_blocks;
   a.softmax_scale = softmax_scale;
+  a.q_start = q_start;
   if (wpa::launch_prefill_attn(a, out_dtype == WPA_BF16, stream) != hipSuccess) return WPA_ERR_LAUNCH;
   return WPA_OK;
 }
 
-wpa_status wpa_mask_counts(int n_tokens, int window_blocks, int sink_blocks, int32_t* counts,
-                           hipStream_t stream) {
-  if (n_tokens < 0 || sink_blocks < 0) return WPA_ERR_SHAPE;
+wpa_status mask_counts(int q_start, int n_tokens, int window_blocks, int sink_blocks, int32_t* counts,
+                       hipStream_t stream) {
+  if (n_tokens < 0 || q_start < 0 || sink_blocks < 0) return WPA_ERR_SHAPE;
+  if ((long)q_start + n_tokens > 0x7fffffffL - WPA_PAGE_TOKENS) return WPA_ERR_UNSUPPORTED;
   if (n_tokens == 0) return WPA_OK;
   if (!counts) return WPA_ERR_NULL;
-  if (wpa::launch_mask_counts(n_tokens, window_blocks, sink_blocks, counts, stream) != hipSuccess)
+  if (wpa::launch_mask_counts(q_start, n_tokens, window_blocks, sink_blocks, counts, stream) != hipSuccess)
     return WPA_ERR_LAUNCH;
   return WPA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+wpa_status wpa_prefill_attn_i8(const int8_t* q_i8, const float* q_scale, const int8_t* k_pool,
+                               const int8_t* v_pool, const float* k_scale, const float* v_scale,
+                               const int32_t* page_table, int n_pool_pages, int n_tokens, int n_q_heads,
+                               int n_kv_heads, int window_blocks, int sink_blocks, float softmax_scale,
+                               void* out, wpa_dtype out_dtype, hipStream_t stream) {
+  return prefill_attn(q_i8, q_scale, k_pool, v_pool, k_scale, v_scale, page_table, n_pool_pages, 0, n_tokens,
+                      n_q_heads, n_kv_heads, window_blocks, sink_blocks, softmax_scale, out, out_dtype, stream);
+}
+
+wpa_status wpa_prefill_attn_i8_chunk(const int8_t* q_i8, const float* q_scale, const int8_t* k_pool,
+                                     const int8_t* v_pool, const float* k_scale, const float* v_scale,
+                                     const int32_t* page_table, int n_pool_pages, int q_start, int n_tokens,
+                                     int n_q_heads, int n_kv_heads, int window_blocks, int sink_blocks,
+                                     float softmax_scale, void* out, wpa_dtype out_dtype, hipStream_t stream) {
+  return prefill_attn(q_i8, q_scale, k_pool, v_pool, k_scale, v_scale, page_table, n_pool_pages, q_start,
+                      n_tokens, n_q_heads, n_kv_heads, window_blocks, sink_blocks, softmax_scale, out, out_dtype,
+                      stream);
+}
+
+wpa_status wpa_mask_counts(int n_tokens, int window_blocks, int sink_blocks, int32_t* counts,
+                           hipStream_t stream) {
+  return mask_counts(0, n_tokens, window_blocks, sink_blocks, counts, stream);
+}
+
+wpa_status wpa_mask_counts_chunk(int q_start, int n_tokens, int window_blocks, int sink_blocks, int32_t* counts,
+                                 hipStream_t stream) {
+  return mask_counts(q_start, n_tokens, window_blocks, sink_blocks, counts, stream);
 }
 
 }  // extern "C"

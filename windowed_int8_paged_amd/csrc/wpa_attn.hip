@@ -434,12 +434,14 @@ __device__ inline void pass2_step(const Stage& st, const v4i (&qf)[HPW][4], int 
   }
 }
 
-// What a wave knows about its work item: workgroup u covers query tile qt,
-// KV head kvh and NW*HPW of its query heads; wave w takes heads
-// head0 .. head0+HPW-1 (16 query rows each).
+// What a wave knows about its work item: workgroup u covers query tile qt
+// (absolute: the call's rows start at tile a.tile0 of the sequence), KV head
+// kvh and NW*HPW of its query heads; wave w takes heads head0 .. head0+HPW-1
+// (16 query rows each).  my_t is the lane's row within the call's Q and out,
+// t_abs its position in the sequence.
 template <int NW, int HPW>
 struct Work {
-  int lane, wave, kvh, qt, head0, my_t;
+  int lane, wave, kvh, qt, qt_local, head0, my_t;
   bool row_ok;
   RowCtx rc;
   TileBlocks tb;
@@ -454,12 +456,13 @@ struct Work {
     const int hg = u % a.hgroups;
     u /= a.hgroups;
     kvh = u % a.n_kv_heads;
-    qt = a.n_tiles - 1 - u / a.n_kv_heads;  // longest tiles first
+    qt_local = a.n_tiles - 1 - u / a.n_kv_heads;  // longest tiles first
+    qt = a.tile0 + qt_local;
     head0 = kvh * a.G + (hg * NW + wave) * HPW;
-    my_t = qt * kPage + (lane & 15);
+    my_t = qt_local * kPage + (lane & 15);
     row_ok = my_t < a.n_tokens;
     rc.g = lane >> 4;
-    rc.t_mask = row_ok ? my_t : a.n_tokens - 1;
+    rc.t_mask = kPage * a.tile0 + (row_ok ? my_t : a.n_tokens - 1);
     tb = tile_blocks(qt, a.window_blocks, a.sink_blocks);
     n_st = (tb.n_total + 3) >> 2;
     kmask = key_mask(tb, n_st - 1, rc);
@@ -608,7 +611,7 @@ __global__ __launch_bounds__(64 * (WPG / HPW), HPW == 2 ? 1 : 2) void prefill_at
     for (int i = 0; i < 4; ++i) {
       const int r = 4 * w.rc.g + i;
       const float rr = __shfl(rscale, r);
-      const int t = w.qt * kPage + r;
+      const int t = w.qt_local * kPage + r;
       if (t >= a.n_tokens) continue;
       const long base = ((long)t * a.n_q_heads + w.head0 + h) * kHeadDim + (w.lane & 15);
 #pragma unroll
@@ -647,6 +650,7 @@ hipError_t launch_prefill_attn(const AttnArgs& args_in, bool out_bf16, hipStream
   const int wpg = a.G % 4 == 0 ? 4 : (a.G % 2 == 0 ? 2 : 1);
   a.hgroups = a.G / wpg;
   a.n_tiles = (a.n_tokens + kPage - 1) / kPage;
+  a.tile0 = a.q_start / kPage;
   a.row_mul = a.softmax_scale * kLog2e;
   const unsigned grid = (unsigned)((long)a.n_tiles * a.n_kv_heads * a.hgroups);
   if (wpg == 4) launch_wpg<4, 1>(a, out_bf16, grid, stream);

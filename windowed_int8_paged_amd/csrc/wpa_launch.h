@@ -18,8 +18,9 @@ struct AttnArgs {
   int n_tokens, n_q_heads, n_kv_heads;
   int window_blocks, sink_blocks;
   float softmax_scale;
+  int q_start;  // sequence position of the call's first query row, a multiple of 16
   // filled in by the launcher
-  int G, hgroups, n_tiles;
+  int G, hgroups, n_tiles, tile0;
   float row_mul;
 };
 
@@ -28,7 +29,7 @@ hipError_t launch_quantize_q_rows(const void* q, bool bf16, int n_tokens, int n_
 hipError_t launch_kv_write(const void* k, const void* v, bool bf16, int n_tokens, int n_kv_heads,
                            const int32_t* slots, int n_pool_pages, int8_t* k_pool, int8_t* v_pool, float* k_scale,
                            float* v_scale, hipStream_t stream);
-hipError_t launch_mask_counts(int n_tokens, int window_blocks, int sink_blocks, int32_t* counts,
+hipError_t launch_mask_counts(int q_start, int n_tokens, int window_blocks, int sink_blocks, int32_t* counts,
                               hipStream_t stream);
 hipError_t launch_prefill_attn(const AttnArgs& args, bool out_bf16, hipStream_t stream);
 

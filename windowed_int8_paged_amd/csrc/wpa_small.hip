@@ -95,15 +95,16 @@ __global__ __launch_bounds__(256) void kv_write_kernel(const void* __restrict__ 
   if (sub == 0) (is_v ? v_scale : k_scale)[dst] = scale;
 }
 
-// counts[t] = number of keys row t attends: every listed block but the
-// diagonal one is attended whole, the diagonal contributes t%16 + 1 keys.
-__global__ __launch_bounds__(256) void mask_counts_kernel(int n_tokens, int window_blocks,
+// counts[i] = number of keys row t = q_start + i attends: every listed block
+// but the diagonal one is attended whole, the diagonal contributes t%16 + 1 keys.
+__global__ __launch_bounds__(256) void mask_counts_kernel(int q_start, int n_tokens, int window_blocks,
                                                           int sink_blocks, int32_t* __restrict__ counts) {
-  const int t = blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= n_tokens) return;
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n_tokens) return;
+  const int t = q_start + i;
   const int qt = t / kPage;
   const TileBlocks tb = tile_blocks(qt, window_blocks, sink_blocks);
-  counts[t] = kPage * (tb.n_total - 1) + (t - kPage * qt + 1);
+  counts[i] = kPage * (tb.n_total - 1) + (t - kPage * qt + 1);
 }
 
 hipError_t launch_quantize_q_rows(const void* q, bool bf16, int n_tokens, int n_q_heads, int8_t* q_i8,
@@ -134,10 +135,10 @@ hipError_t launch_kv_write(const void* k, const void* v, bool bf16, int n_tokens
   return hipGetLastError();
 }
 
-hipError_t launch_mask_counts(int n_tokens, int window_blocks, int sink_blocks, int32_t* counts,
+hipError_t launch_mask_counts(int q_start, int n_tokens, int window_blocks, int sink_blocks, int32_t* counts,
                               hipStream_t stream) {
   const unsigned blocks = (unsigned)((n_tokens + 255) / 256);
-  hipLaunchKernelGGL(mask_counts_kernel, dim3(blocks), dim3(256), 0, stream, n_tokens, window_blocks,
+  hipLaunchKernelGGL(mask_counts_kernel, dim3(blocks), dim3(256), 0, stream, q_start, n_tokens, window_blocks,
                      sink_blocks, counts);
   return hipGetLastError();
 }
