@@ -223,6 +223,82 @@ def bench_chunk(args):
     print(json.dumps(res), flush=True)
 
 
+def bench_decode(args):
+    """Split-KV decode: one new token for each of 64 sequences at position 32767
+    (16 q heads / 4 kv heads, window 256 blocks + 1 sink block), each sequence
+    owning the 257 pages its token attends.  HBM-bound: the roofline is the K
+    and V rows plus scales of every attended key (plus Q and out)."""
+    import numpy as np
+    import torch
+    import windowed_int8_paged_amd as wpa
+    import workloads
+
+    B, L, hq, hkv, W, S = 64, 32768, 16, 4, 256, 1
+    d = workloads.make_decode_batch([L] * B, hq, hkv, W, S, seed=1007, attended_pages_only=True)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    q = torch.from_numpy(d.q_bf16.view(np.int16)).cuda().view(torch.bfloat16)
+    kp, vp, ks, vs = dev(d.k_pool), dev(d.v_pool), dev(d.k_scale), dev(d.v_scale)
+    tables, lens = dev(d.page_tables), dev(d.seq_lens)
+    q_i8 = torch.empty((B, hq, 256), dtype=torch.int8, device="cuda")
+    q_scale = torch.empty((B, hq), dtype=torch.float32, device="cuda")
+    out = torch.empty((B, hq, 256), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty((wpa.decode_workspace_bytes(B, hq, tables.shape[1], W, S),), dtype=torch.uint8, device="cuda")
+    keys = int(wpa.mask_counts_chunk(L - 1, 1, W, S).item())  # keys the last position attends
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        wpa.quantize_q_rows(q, q_i8, q_scale)
+        if ev is not None:
+            ev[1].record()
+        wpa.decode_attn_i8(q_i8, q_scale, kp, vp, ks, vs, tables, lens, W, S, d.softmax_scale, out=out,
+                           workspace=ws)
+        if ev is not None:
+            ev[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    dec_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    quant_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    nbytes = B * keys * hkv * (2 * 256 + 2 * 4) + B * hq * (256 + 4) + B * hq * 256 * 2
+    gbs = nbytes / (dec_ms * 1e-3) / 1e9
+    res = {
+        "metric": "decode GB/s (int8 split-KV decode over the paged pool, one token for each of 64 sequences)",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int8", "data": "synthetic",
+        "config": {"workload": f"decode, {B} sequences at position {L - 1}, {hq} q heads / {hkv} kv heads, window "
+                               f"{W} blocks + {S} sink block, each sequence owning its {keys // 16} attended pages",
+                   "attended_keys_per_sequence": keys, "bytes_per_step": nbytes,
+                   "tokens_per_s": round(B / (wall / args.steps), 1)},
+        "kernel_ms": {"quantize_q_rows": round(quant_ms, 4), "decode_attn_i8": round(dec_ms, 4)},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "decode_attn_i8"},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        t1, done = time.perf_counter(), 0
+        for b in range(B):
+            case = workloads.decode_row_case(d, b)
+            oracle.attention_int8_mirror(case, tiles=[(L - 1) // 16])
+            done += 1
+            if time.perf_counter() - t1 >= args.cpu_seconds:
+                break
+        dt = time.perf_counter() - t1
+        cb = done * keys * hkv * (2 * 256 + 2 * 4)
+        res["cpu_baseline"] = {"value": round(cb / dt / 1e9, 4), "unit": "GB/s", "cores": blas_threads(),
+                               "kind": "oracle", "sample": f"int8-mirror oracle, {done} of {B} sequences (a whole "
+                                                           f"16-row tile each), {dt:.1f} s"}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -232,9 +308,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true")
-    ap.add_argument("--op", choices=["attention", "kv_write", "chunk"], default="attention",
+    ap.add_argument("--op", choices=["attention", "kv_write", "chunk", "decode"], default="attention",
                     help="attention: the headline step; kv_write: the KV-pool writer at the 32k shape; "
-                         "chunk: a 4096-row prefill chunk at position 65536 over a 69632-token cache")
+                         "chunk: a 4096-row prefill chunk at position 65536 over a 69632-token cache; "
+                         "decode: one token for each of 64 sequences at position 32767")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -254,6 +331,9 @@ def main():
         return
     if args.op == "chunk":
         bench_chunk(args)
+        return
+    if args.op == "decode":
+        bench_decode(args)
         return
 
     import windowed_int8_paged_amd as wpa

@@ -27,6 +27,7 @@
 #ifndef WPA_H
 #define WPA_H
 
+#include <stddef.h>
 #include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
@@ -188,6 +189,52 @@ wpa_status wpa_mask_counts_chunk(int q_start, int n_tokens, int window_blocks, i
 wpa_status wpa_kv_write_i8(const void* k, const void* v, wpa_dtype dtype, int n_tokens, int n_kv_heads,
                            const int32_t* slots, int n_pool_pages, int8_t* k_pool, int8_t* v_pool,
                            float* k_scale, float* v_scale, hipStream_t stream);
+
+/*
+ * Split-KV decode: one new query token per sequence over the paged int8 pool,
+ * with the prefill path's mask and int8 scheme (int8 tensor-core prefill
+ * attention page, "Why the attention, and why tensor cores", which credits
+ * the scheme to the int8 GQA flash-decode; "Relation to open PRs").  Sequence
+ * b has seq_lens[b] tokens in the pool, the last of which is the query:
+ * position t = seq_lens[b] - 1 attends A(t) as defined for
+ * wpa_prefill_attn_i8, through its own page table.  Per (sequence, head) the
+ * output is the same formula (row Q scale, per-token K scale, softmax scale
+ * on the int32 QK^T; v_scale folded into P; P quantized per 16-key block;
+ * int8 PV; l from the unquantized P), up to float32 rounding.
+ *
+ *   q_i8, q_scale  [batch][n_q_heads][256] int8 and [batch][n_q_heads] float32
+ *                  (wpa_quantize_q_rows with n_tokens = batch); q_i8 16-byte aligned.
+ *   k_pool, v_pool, k_scale, v_scale  as for wpa_prefill_attn_i8
+ *                  (n_pool_pages pages), pools 16-byte aligned.
+ *   page_tables    [batch][max_blocks] int32, device: block -> physical page
+ *                  of each sequence.  Entries of attended blocks should lie in
+ *                  [0, n_pool_pages); others are clamped into it (a wrong
+ *                  entry reads a wrong page, never outside the pool).
+ *   seq_lens       [batch] int32, device; a length above 16*max_blocks is
+ *                  taken as 16*max_blocks, and a length <= 0 gives a zero row.
+ *   n_q_heads / n_kv_heads must be at most 16.
+ *   workspace      device scratch of at least wpa_decode_workspace_bytes(...)
+ *                  bytes, 16-byte aligned, owned by the caller; its contents
+ *                  on entry do not matter.  Calls that share a workspace
+ *                  must be ordered on one stream.
+ *   out            [batch][n_q_heads][256], WPA_BF16 (rounded to nearest
+ *                  even) or WPA_F32.
+ * Errors: NULL pointer -> WPA_ERR_NULL; batch < 0, heads <= 0,
+ * n_q_heads % n_kv_heads != 0, max_blocks <= 0, n_pool_pages <= 0,
+ * sink_blocks < 0, softmax_scale not finite or <= 0, or a workspace smaller
+ * than needed -> WPA_ERR_SHAPE; other dtype, misalignment or more than 16
+ * query heads per KV head -> WPA_ERR_UNSUPPORTED.
+ */
+size_t wpa_decode_workspace_bytes(int batch, int n_q_heads, int max_blocks, int window_blocks,
+                                  int sink_blocks);
+wpa_status wpa_decode_attn_i8(const int8_t* q_i8, const float* q_scale,
+                              const int8_t* k_pool, const int8_t* v_pool,
+                              const float* k_scale, const float* v_scale, int n_pool_pages,
+                              const int32_t* page_tables, int max_blocks, const int32_t* seq_lens,
+                              int batch, int n_q_heads, int n_kv_heads,
+                              int window_blocks, int sink_blocks, float softmax_scale,
+                              void* workspace, size_t workspace_bytes,
+                              void* out, wpa_dtype out_dtype, hipStream_t stream);
 
 /* Static, human-readable name of a status ("WPA_OK", ...; "unknown status"). */
 const char* wpa_status_string(wpa_status s);

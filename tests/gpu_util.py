@@ -45,12 +45,15 @@ def rows_of_tiles(n_tokens, tiles):
     return np.concatenate([oracle.tile_rows(n_tokens, t) for t in tiles])
 
 
-def check_parity(case, out, tiles=None, label=""):
+def check_parity(case, out, tiles=None, label="", rows=None):
     """Compare a GPU output (torch, [N][Hq][256]) with both oracle modes on the
-    rows of `tiles` (all tiles when None).  Returns the measured errors."""
+    rows of `tiles` (all tiles when None), or only on `rows` of those tiles.
+    Returns the measured errors."""
     n_tiles = (case.n_tokens + 15) // 16
     tiles = list(range(n_tiles)) if tiles is None else sorted(set(tiles))
-    rows = rows_of_tiles(case.n_tokens, tiles)
+    if rows is None:
+        rows = rows_of_tiles(case.n_tokens, tiles)
+    rows = np.asarray(rows)
     o = out.float().cpu().numpy()[rows].astype(np.float64)
     b, slack = oracle.attention_int8_mirror(case, tiles=tiles, tie_slack=True)
     b, slack = b[rows], slack[rows]

@@ -32,6 +32,10 @@ def lib():
     L.wpa_kv_write_i8.argtypes = [vp, vp, ci, ci, ci, vp, ci, vp, vp, vp, vp, vp]
     L.wpa_prefill_attn_i8_chunk.argtypes = [vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, cf, vp, ci, vp]
     L.wpa_mask_counts_chunk.argtypes = [ci, ci, ci, ci, vp, vp]
+    L.wpa_decode_workspace_bytes.argtypes = [ci, ci, ci, ci, ci]
+    L.wpa_decode_workspace_bytes.restype = ctypes.c_size_t
+    L.wpa_decode_attn_i8.argtypes = [vp, vp, vp, vp, vp, vp, ci, vp, ci, vp, ci, ci, ci, ci, ci, cf, vp,
+                                     ctypes.c_size_t, vp, ci, vp]
     L.wpa_status_string.argtypes = [ci]
     L.wpa_status_string.restype = ctypes.c_char_p
     return L
@@ -40,7 +44,8 @@ def lib():
 def test_header_declares_the_entry_points():
     fns = declared_functions()
     for f in ("wpa_quantize_q_rows", "wpa_prefill_attn_i8", "wpa_mask_counts", "wpa_kv_write_i8",
-              "wpa_prefill_attn_i8_chunk", "wpa_mask_counts_chunk", "wpa_status_string"):
+              "wpa_prefill_attn_i8_chunk", "wpa_mask_counts_chunk", "wpa_decode_attn_i8",
+              "wpa_decode_workspace_bytes", "wpa_status_string"):
         assert f in fns
 
 
@@ -150,6 +155,38 @@ def test_chunk_entry_points_reject_invalid_arguments(lib):
     assert m(16, -1, 4, 1, P, None) == SHAPE
     assert m(16, 10, 4, 1, None, None) == NULL
     assert m(16, 0, 4, 1, None, None) == OK
+
+
+def test_decode_workspace_size(lib):
+    ws = lib.wpa_decode_workspace_bytes
+    # splits of 8 pages over the longest key list the tables allow: 260 floats per (sequence, head, split)
+    assert ws(3, 8, 100, 0, 0) == 3 * 8 * 13 * 260 * 4       # full causal: 100 blocks -> 13 splits
+    assert ws(3, 8, 2048, 256, 1) == 3 * 8 * 33 * 260 * 4    # window: 257 blocks -> 33 splits
+    assert ws(3, 8, 5, 256, 1) == 3 * 8 * 1 * 260 * 4
+    assert ws(0, 8, 5, 0, 0) == 0
+
+
+def test_decode_rejects_invalid_arguments(lib):
+    need = lib.wpa_decode_workspace_bytes(2, 8, 10, 4, 1)
+
+    def d(q=P, n_pool=4, pt=P, max_blocks=10, lens=P, batch=2, hq=8, hkv=2, W=4, S=1, scale=0.0625, ws=P,
+          ws_bytes=None, out=P, dtype=1):
+        return lib.wpa_decode_attn_i8(q, P, P, P, P, P, n_pool, pt, max_blocks, lens, batch, hq, hkv, W, S, scale,
+                                      ws, need if ws_bytes is None else ws_bytes, out, dtype, None)
+    assert d(batch=-1) == SHAPE
+    assert d(hq=6, hkv=4) == SHAPE
+    assert d(max_blocks=0) == SHAPE
+    assert d(n_pool=0) == SHAPE
+    assert d(S=-1) == SHAPE
+    assert d(scale=0.0) == SHAPE
+    assert d(ws_bytes=need - 1) == SHAPE
+    assert d(dtype=9) == UNSUP
+    assert d(hq=34, hkv=2) == UNSUP       # 17 query heads per KV head
+    assert d(q=None) == NULL
+    assert d(lens=None) == NULL
+    assert d(ws=None) == NULL
+    assert d(ws=ctypes.c_void_p(0x100004)) == UNSUP
+    assert d(batch=0, q=None, lens=None, ws=None, out=None) == OK
 
 
 def test_host_block_list_matches_oracle_counts():

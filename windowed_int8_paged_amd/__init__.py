@@ -13,6 +13,9 @@ Entry points mirror the C ABI in include/wpa.h:
     kv_write_i8(k, v, slots, k_pool, v_pool, k_scale, v_scale)  (writes the pools in place)
     prefill_attn_i8_chunk(q_start, q_i8, q_scale, ...same as prefill_attn_i8...) -> out
     mask_counts_chunk(q_start, n_tokens, window_blocks, sink_blocks, counts=None, device=None) -> counts
+    decode_attn_i8(q_i8, q_scale, k_pool, v_pool, k_scale, v_scale, page_tables, seq_lens,
+                   window_blocks, sink_blocks, softmax_scale, out=None, out_dtype=torch.bfloat16,
+                   workspace=None)                     -> out
 """
 from __future__ import annotations
 
@@ -22,7 +25,7 @@ import os
 import torch
 
 __all__ = ["quantize_q_rows", "prefill_attn_i8", "prefill_attn_i8_chunk", "mask_counts", "mask_counts_chunk",
-           "kv_write_i8", "lib", "LIB_PATH",
+           "kv_write_i8", "decode_attn_i8", "decode_workspace_bytes", "lib", "LIB_PATH",
            "HEAD_DIM", "PAGE_TOKENS", "WpaError"]
 
 HEAD_DIM = 256
@@ -51,6 +54,11 @@ def _load():
     L.wpa_prefill_attn_i8_chunk.restype = ci
     L.wpa_mask_counts_chunk.argtypes = [ci, ci, ci, ci, vp, vp]
     L.wpa_mask_counts_chunk.restype = ci
+    L.wpa_decode_workspace_bytes.argtypes = [ci, ci, ci, ci, ci]
+    L.wpa_decode_workspace_bytes.restype = ctypes.c_size_t
+    L.wpa_decode_attn_i8.argtypes = [vp, vp, vp, vp, vp, vp, ci, vp, ci, vp, ci, ci, ci, ci, ci, cf, vp,
+                                     ctypes.c_size_t, vp, ci, vp]
+    L.wpa_decode_attn_i8.restype = ci
     L.wpa_kv_write_i8.argtypes = [vp, vp, ci, ci, ci, vp, ci, vp, vp, vp, vp, vp]
     L.wpa_kv_write_i8.restype = ci
     L.wpa_status_string.argtypes = [ci]
@@ -190,3 +198,46 @@ def kv_write_i8(k, v, slots, k_pool, v_pool, k_scale, v_scale):
     _check(lib.wpa_kv_write_i8(_ptr(k), _ptr(v), WPA_BF16 if k.dtype == torch.bfloat16 else WPA_F32, n, hkv,
                                _ptr(slots), n_pool, _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale),
                                _stream(k.device)))
+
+
+def decode_workspace_bytes(batch, n_q_heads, max_blocks, window_blocks, sink_blocks):
+    return int(lib.wpa_decode_workspace_bytes(int(batch), int(n_q_heads), int(max_blocks), int(window_blocks),
+                                              int(sink_blocks)))
+
+
+def decode_attn_i8(q_i8, q_scale, k_pool, v_pool, k_scale, v_scale, page_tables, seq_lens,
+                   window_blocks, sink_blocks, softmax_scale, out=None, out_dtype=torch.bfloat16, workspace=None):
+    """One query token per sequence (its last position) over the paged pool;
+    see include/wpa.h.  page_tables: int32 [batch][max_blocks]; seq_lens: int32 [batch]."""
+    _dev(q_i8, "q_i8", torch.int8)
+    batch, hq, d = q_i8.shape
+    if d != HEAD_DIM:
+        raise ValueError("head_dim must be 256")
+    _dev(q_scale, "q_scale", torch.float32, (batch, hq))
+    _dev(k_pool, "k_pool", torch.int8)
+    n_pool, page, hkv, d2 = k_pool.shape
+    if page != PAGE_TOKENS or d2 != HEAD_DIM:
+        raise ValueError("pool pages must be [16][n_kv_heads][256]")
+    _dev(v_pool, "v_pool", torch.int8, k_pool.shape)
+    _dev(k_scale, "k_scale", torch.float32, (n_pool, page, hkv))
+    _dev(v_scale, "v_scale", torch.float32, (n_pool, page, hkv))
+    _dev(page_tables, "page_tables", torch.int32)
+    if page_tables.dim() != 2 or page_tables.shape[0] != batch:
+        raise ValueError("page_tables must be [batch][max_blocks]")
+    max_blocks = page_tables.shape[1]
+    _dev(seq_lens, "seq_lens", torch.int32, (batch,))
+    need = decode_workspace_bytes(batch, hq, max_blocks, window_blocks, sink_blocks)
+    if workspace is None:
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=q_i8.device)
+    _dev(workspace, "workspace", torch.uint8)
+    if out is None:
+        out = torch.empty((batch, hq, d), dtype=out_dtype, device=q_i8.device)
+    if out.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("out must be bfloat16 or float32")
+    _dev(out, "out", out.dtype, (batch, hq, d))
+    _check(lib.wpa_decode_attn_i8(
+        _ptr(q_i8), _ptr(q_scale), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale), n_pool,
+        _ptr(page_tables), max_blocks, _ptr(seq_lens), batch, hq, hkv, int(window_blocks), int(sink_blocks),
+        float(softmax_scale), _ptr(workspace), workspace.numel(), _ptr(out),
+        WPA_BF16 if out.dtype == torch.bfloat16 else WPA_F32, _stream(q_i8.device)))
+    return out

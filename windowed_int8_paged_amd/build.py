@@ -14,7 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libwpa.so")
-SOURCES = ["wpa_api.cpp", "wpa_small.hip", "wpa_attn.hip"]
+SOURCES = ["wpa_api.cpp", "wpa_small.hip", "wpa_attn.hip", "wpa_decode.hip"]
 
 # Packed fp32 VALU ops are disabled for every device pass (the host pass warns
 # that it does not know the feature; that is harmless).

@@ -148,6 +148,57 @@ wpa_status wpa_mask_counts(int n_tokens, int window_blocks, int sink_blocks, int
   return mask_counts(0, n_tokens, window_blocks, sink_blocks, counts, stream);
 }
 
+size_t wpa_decode_workspace_bytes(int batch, int n_q_heads, int max_blocks, int window_blocks, int sink_blocks) {
+  if (batch <= 0 || n_q_heads <= 0 || max_blocks <= 0) return 0;
+  const int splits = wpa::decode_splits(max_blocks, window_blocks, sink_blocks < 0 ? 0 : sink_blocks);
+  return (size_t)batch * n_q_heads * splits * wpa::kWsRow * sizeof(float);
+}
+
+wpa_status wpa_decode_attn_i8(const int8_t* q_i8, const float* q_scale, const int8_t* k_pool, const int8_t* v_pool,
+                              const float* k_scale, const float* v_scale, int n_pool_pages,
+                              const int32_t* page_tables, int max_blocks, const int32_t* seq_lens, int batch,
+                              int n_q_heads, int n_kv_heads, int window_blocks, int sink_blocks, float softmax_scale,
+                              void* workspace, size_t workspace_bytes, void* out, wpa_dtype out_dtype,
+                              hipStream_t stream) {
+  if (batch < 0 || n_q_heads <= 0 || n_kv_heads <= 0 || n_q_heads % n_kv_heads != 0) return WPA_ERR_SHAPE;
+  if (max_blocks <= 0 || n_pool_pages <= 0 || sink_blocks < 0) return WPA_ERR_SHAPE;
+  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return WPA_ERR_SHAPE;
+  if (out_dtype != WPA_BF16 && out_dtype != WPA_F32) return WPA_ERR_UNSUPPORTED;
+  if (n_q_heads / n_kv_heads > wpa::kMaxDecodeG) return WPA_ERR_UNSUPPORTED;
+  if (batch == 0) return WPA_OK;
+  if (!q_i8 || !q_scale || !k_pool || !v_pool || !k_scale || !v_scale || !page_tables || !seq_lens || !workspace ||
+      !out)
+    return WPA_ERR_NULL;
+  if (workspace_bytes < wpa_decode_workspace_bytes(batch, n_q_heads, max_blocks, window_blocks, sink_blocks))
+    return WPA_ERR_SHAPE;
+  if (!aligned16(q_i8) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(workspace))
+    return WPA_ERR_UNSUPPORTED;
+  const long splits = wpa::decode_splits(max_blocks, window_blocks, sink_blocks);
+  if ((long)batch * n_kv_heads * splits > 0x7fffffffL || (long)batch * n_q_heads > 0x7fffffffL)
+    return WPA_ERR_UNSUPPORTED;
+  wpa::DecodeArgs a = {};
+  a.q_i8 = q_i8;
+  a.q_scale = q_scale;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.page_tables = page_tables;
+  a.seq_lens = seq_lens;
+  a.ws = static_cast<float*>(workspace);
+  a.out = out;
+  a.n_pool_pages = n_pool_pages;
+  a.max_blocks = max_blocks;
+  a.batch = batch;
+  a.n_q_heads = n_q_heads;
+  a.n_kv_heads = n_kv_heads;
+  a.window_blocks = window_blocks;
+  a.sink_blocks = sink_blocks;
+  a.softmax_scale = softmax_scale;
+  if (wpa::launch_decode(a, out_dtype == WPA_BF16, stream) != hipSuccess) return WPA_ERR_LAUNCH;
+  return WPA_OK;
+}
+
 wpa_status wpa_mask_counts_chunk(int q_start, int n_tokens, int window_blocks, int sink_blocks, int32_t* counts,
                                  hipStream_t stream) {
   return mask_counts(q_start, n_tokens, window_blocks, sink_blocks, counts, stream);

@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <algorithm>
 #include <stdint.h>
 
 namespace wpa {
@@ -23,6 +24,30 @@ struct AttnArgs {
   int G, hgroups, n_tiles, tile0;
   float row_mul;
 };
+
+// Split-KV decode (wpa_decode.hip).
+constexpr int kMaxDecodeG = 16;  // query heads per KV head
+constexpr int kWsRow = 260;      // floats per (sequence, head, split): O[256], Z, l, 2 pad (16-byte rows)
+struct DecodeArgs {
+  const int8_t* q_i8;
+  const float* q_scale;
+  const int8_t* k_pool;
+  const int8_t* v_pool;
+  const float* k_scale;
+  const float* v_scale;
+  const int32_t* page_tables;
+  const int32_t* seq_lens;
+  float* ws;
+  void* out;
+  int n_pool_pages, max_blocks, batch, n_q_heads, n_kv_heads;
+  int window_blocks, sink_blocks;
+  float softmax_scale;
+  // filled in by the launcher
+  int G, n_splits;
+  float row_mul;
+};
+int decode_splits(int max_blocks, int window_blocks, int sink_blocks);
+hipError_t launch_decode(const DecodeArgs& args, bool out_bf16, hipStream_t stream);
 
 hipError_t launch_quantize_q_rows(const void* q, bool bf16, int n_tokens, int n_q_heads, int8_t* q_i8,
                                   float* q_scale, hipStream_t stream);

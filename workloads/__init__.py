@@ -30,7 +30,7 @@ import numpy as np
 HEAD_DIM = 256
 PAGE = 16
 
-__all__ = ["Case", "CONFIGS", "make_config", "make_case", "make_kv_rows", "HEAD_DIM", "PAGE"]
+__all__ = ["Case", "CONFIGS", "make_config", "make_case", "make_kv_rows", "make_decode_batch", "decode_row_case", "HEAD_DIM", "PAGE"]
 
 
 @dataclasses.dataclass
@@ -204,3 +204,87 @@ def make_kv_rows(n_tokens: int, n_kv_heads: int, n_pool_pages: int, seed: int):
     v_scale = rng.uniform(0.005, 0.02, size=(n_pool_pages, PAGE, n_kv_heads)).astype(np.float32)
     kb, vb = _round_to_bf16_bits(k), _round_to_bf16_bits(v)
     return (kb, vb, _bf16_bits_to_f32(kb), _bf16_bits_to_f32(vb), slots, k_pool, v_pool, k_scale, v_scale)
+
+
+@dataclasses.dataclass
+class DecodeBatch:
+    """Inputs of one decode step: sequence b has seq_lens[b] tokens in the pool and
+    its last position is the query q[b]."""
+    n_q_heads: int
+    n_kv_heads: int
+    window_blocks: int
+    sink_blocks: int
+    softmax_scale: float
+    q_bf16: np.ndarray        # uint16 [batch][n_q_heads][256]
+    q_f32: np.ndarray         # float32, the exact widening
+    k_pool: np.ndarray
+    v_pool: np.ndarray
+    k_scale: np.ndarray
+    v_scale: np.ndarray
+    page_tables: np.ndarray   # int32 [batch][max_blocks]; -1 past each sequence's last block
+    seq_lens: np.ndarray      # int32 [batch]
+
+
+def make_decode_batch(seq_lens, n_q_heads: int, n_kv_heads: int, window_blocks: int, sink_blocks: int,
+                      seed: int, max_blocks: int | None = None, attended_pages_only: bool = False,
+                      softmax_scale: float = 1.0 / 16.0) -> DecodeBatch:
+    """Seeded decode inputs.  Draw order: Q, pool codes (K, V), scales (K, V), page maps.
+
+    By default every sequence maps its blocks to a seeded random choice of
+    distinct pool pages out of a pool as large as the longest sequence needs
+    (sequences may share pages).  With attended_pages_only, each sequence owns
+    fresh pages for exactly the blocks its last position attends (sink and
+    window blocks) and maps every other block to page 0, which is never read:
+    the whole pool is then what one decode step must stream."""
+    seq_lens = np.asarray(seq_lens, dtype=np.int32)
+    batch = len(seq_lens)
+    rng = np.random.default_rng(seed)
+    need = [(int(L) + PAGE - 1) // PAGE for L in seq_lens]
+    max_blocks = max_blocks or max(max(need), 1)
+    q = rng.standard_normal((batch, n_q_heads, HEAD_DIM), dtype=np.float32)
+    if attended_pages_only:
+        lists = []
+        for L in seq_lens:
+            t = int(L) - 1
+            qt = t // PAGE
+            if window_blocks <= 0:
+                blocks = list(range(qt + 1))
+            else:
+                rsb = max(0, qt + 1 - window_blocks)
+                blocks = list(range(min(sink_blocks, rsb))) + list(range(rsb, qt + 1))
+            lists.append(blocks)
+        n_pool = 1 + sum(len(b) for b in lists)
+    else:
+        n_pool = max_blocks
+    k_pool = rng.integers(-127, 128, size=(n_pool, PAGE, n_kv_heads, HEAD_DIM), dtype=np.int8)
+    v_pool = rng.integers(-127, 128, size=(n_pool, PAGE, n_kv_heads, HEAD_DIM), dtype=np.int8)
+    k_scale = rng.uniform(0.005, 0.02, size=(n_pool, PAGE, n_kv_heads)).astype(np.float32)
+    v_scale = rng.uniform(0.005, 0.02, size=(n_pool, PAGE, n_kv_heads)).astype(np.float32)
+    tables = np.full((batch, max_blocks), -1, dtype=np.int32)
+    if attended_pages_only:
+        nxt = 1
+        for b, blocks in enumerate(lists):
+            tables[b, :need[b]] = 0
+            fresh = rng.permutation(len(blocks)).astype(np.int32) + nxt
+            tables[b, blocks] = fresh
+            nxt += len(blocks)
+    else:
+        for b in range(batch):
+            tables[b, :need[b]] = rng.permutation(n_pool)[:need[b]]
+    qb = _round_to_bf16_bits(q)
+    return DecodeBatch(n_q_heads, n_kv_heads, window_blocks, sink_blocks, softmax_scale, qb,
+                       _bf16_bits_to_f32(qb), k_pool, v_pool, k_scale, v_scale, tables, seq_lens)
+
+
+def decode_row_case(batch: DecodeBatch, b: int) -> Case:
+    """Sequence b of a decode batch as a prefill case whose row seq_lens[b]-1 is
+    the decode query (all other rows zero), for evaluating the oracle there."""
+    L = int(batch.seq_lens[b])
+    qf = np.zeros((L, batch.n_q_heads, HEAD_DIM), dtype=np.float32)
+    qb = np.zeros((L, batch.n_q_heads, HEAD_DIM), dtype=np.uint16)
+    qf[L - 1], qb[L - 1] = batch.q_f32[b], batch.q_bf16[b]
+    table = batch.page_tables[b, :(L + PAGE - 1) // PAGE].copy()
+    return Case(name=f"decode{b}", n_tokens=L, n_q_heads=batch.n_q_heads, n_kv_heads=batch.n_kv_heads,
+                window_blocks=batch.window_blocks, sink_blocks=batch.sink_blocks,
+                softmax_scale=batch.softmax_scale, out_dtype="f32", q_bf16=qb, q_f32=qf, k_pool=batch.k_pool,
+                v_pool=batch.v_pool, k_scale=batch.k_scale, v_scale=batch.v_scale, page_table=table, seed=0)
