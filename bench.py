@@ -56,6 +56,23 @@ def copy_calibration(steps: int) -> None:
     print(json.dumps({"copy_calibration_bytes_per_direction": n, "launches": steps}), flush=True)
 
 
+def warm_up(step, args) -> None:
+    """The W counted warmup steps, then further untimed steps, queued back to
+    back, until args.settle_ms of wall time has passed.  The GPU's clocks rise
+    only under continuous load: after an idle gap the first ten or so steps
+    of the 32k attention run up to 20% slower (measured per step with HIP
+    events), and steps separated by host synchronizations do not settle them."""
+    import torch
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < args.settle_ms:
+        for _ in range(8):
+            step()
+        torch.cuda.synchronize()
+
+
 def blas_threads() -> int:
     """Threads the oracle's numpy BLAS calls run on."""
     try:
@@ -110,9 +127,7 @@ def bench_kv_write(args):
     k, v, sl = bf(kb), bf(vb), dev(slots)
     kp, vp, ks, vs = dev(kp), dev(vp), dev(ks), dev(vs)
     call = lambda: wpa.kv_write_i8(k, v, sl, kp, vp, ks, vs)
-    for _ in range(args.warmup):
-        call()
-    torch.cuda.synchronize()
+    warm_up(call, args)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     t0 = time.perf_counter()
     for e0, e1 in evs:
@@ -126,7 +141,7 @@ def bench_kv_write(args):
     gbs = nbytes / (ms * 1e-3) / 1e9
     res = {
         "metric": "KV-pool write GB/s (bf16 K/V rows -> int8 pool pages + per-token scales)",
-        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "settle_ms": args.settle_ms,
         "ms_per_step": round(wall * 1e3 / args.steps, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16->int8", "data": "synthetic",
         "config": {"workload": f"KV-pool write, {n} tokens x {hkv} KV heads x 256 bf16 K and V into a "
@@ -182,9 +197,7 @@ def bench_chunk(args):
         if ev is not None:
             ev[2].record()
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_up(step, args)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     t0 = time.perf_counter()
     for e in evs:
@@ -197,7 +210,7 @@ def bench_chunk(args):
     res = {
         "metric": "int8 TOPS, hd256 windowed prefill attn, 4096-row chunk at position 65536",
         "value": round(ops / (ms * 1e-3) / 1e12, 2), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "warmup": args.warmup, "settle_ms": args.settle_ms, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "int8", "data": "synthetic",
         "config": {"workload": "chunked prefill: query rows 65536..69631 of a 69632-token sequence, 16 q heads / "
                                "4 kv heads, window 256 blocks + 1 sink block, int8 paged pool of 4352 shuffled "
@@ -256,9 +269,7 @@ def bench_decode(args):
         if ev is not None:
             ev[2].record()
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_up(step, args)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     t0 = time.perf_counter()
     for e in evs:
@@ -271,7 +282,7 @@ def bench_decode(args):
     gbs = nbytes / (dec_ms * 1e-3) / 1e9
     res = {
         "metric": "decode GB/s (int8 split-KV decode over the paged pool, one token for each of 64 sequences)",
-        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "settle_ms": args.settle_ms,
         "ms_per_step": round(wall * 1e3 / args.steps, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "int8", "data": "synthetic",
         "config": {"workload": f"decode, {B} sequences at position {L - 1}, {hq} q heads / {hkv} kv heads, window "
@@ -304,10 +315,16 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--settle-ms", type=float, default=500.0,
+                    help="after the warmup steps, further untimed steps for this long (clock settling)")
     ap.add_argument("--config", default="32k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--q-path", choices=["fused", "separate"], default="fused",
+                    help="attention: fused = wpa_prefill_attn_fused_q (Q quantized inside the attention kernels); "
+                         "separate = wpa_quantize_q_rows then wpa_prefill_attn_i8.  The other path is timed "
+                         "after the main steps and reported beside them")
     ap.add_argument("--op", choices=["attention", "kv_write", "chunk", "decode"], default="attention",
                     help="attention: the headline step; kv_write: the KV-pool writer at the 32k shape; "
                          "chunk: a 4096-row prefill chunk at position 65536 over a 69632-token cache; "
@@ -351,39 +368,81 @@ def main():
     out = torch.empty((N, Hq, 256), dtype=torch.bfloat16, device="cuda")
     counts = torch.empty((N,), dtype=torch.int32, device="cuda")
 
-    def step(ev=None):
+    def attn(ev=None):
+        wpa.prefill_attn_i8(q_i8, q_scale, k_pool, v_pool, k_scale, v_scale, page_table,
+                            case.window_blocks, case.sink_blocks, case.softmax_scale, out=out)
+
+    def step_separate(ev=None):
         if ev is not None:
             ev[0].record()
         wpa.quantize_q_rows(q, q_i8, q_scale)
         if ev is not None:
             ev[1].record()
-        wpa.prefill_attn_i8(q_i8, q_scale, k_pool, v_pool, k_scale, v_scale, page_table,
-                            case.window_blocks, case.sink_blocks, case.softmax_scale, out=out)
+        attn()
         if ev is not None:
             ev[2].record()
         wpa.mask_counts(N, case.window_blocks, case.sink_blocks, counts=counts)
         if ev is not None:
             ev[3].record()
 
-    for _ in range(args.warmup):
-        step()
+    def step_fused(ev=None):
+        if ev is not None:
+            ev[0].record()
+            ev[1].record()
+        wpa.prefill_attn_fused_q(q, k_pool, v_pool, k_scale, v_scale, page_table, case.window_blocks,
+                                 case.sink_blocks, case.softmax_scale, out=out)
+        if ev is not None:
+            ev[2].record()
+        wpa.mask_counts(N, case.window_blocks, case.sink_blocks, counts=counts)
+        if ev is not None:
+            ev[3].record()
+
+    def attn_only(ev=None):
+        if ev is not None:
+            ev[0].record()
+            ev[1].record()
+        attn()
+        if ev is not None:
+            ev[2].record()
+            ev[3].record()
+
+    def timed(step, n):
+        """Wall-clock ms per step over n steps, and the mean HIP-event spans
+        (quantize, attention, mask counts) of a step."""
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(n):
+            step(evs[i])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        spans = [float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) for j in range(3)]
+        per_step = [e[0].elapsed_time(e[3]) for e in evs]
+        print(f"[bench] {step.__name__}: step ms " + " ".join(f"{x:.3f}" for x in per_step),
+              file=sys.stderr, flush=True)
+        return wall * 1e3 / n, spans
+
+    main_step, other_step = ((step_fused, step_separate) if args.q_path == "fused"
+                             else (step_separate, step_fused))
+    other_step()
     torch.cuda.synchronize()
+    # before the warm-up: the first torch reduction loads its kernels, a pause
+    # long enough for the clocks to drop again
     total_keys = int(counts.to(torch.int64).sum().item())
     ops = 4.0 * total_keys * 256 * Hq
+    warm_up(main_step, args)
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    quant_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    attn_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
-    mask_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
-    ms_per_step = wall * 1e3 / args.steps
+    # the timed steps of the chosen user path, then (untimed for `value`) the
+    # int8-Q attention launch alone, the roofline kernel, and the other path
+    ms_per_step, (quant_ms, main_attn_ms, mask_ms) = timed(main_step, args.steps)
+    attn_ms = timed(attn_only, args.steps)[1][1]
+    other_ms, (other_quant_ms, other_attn_ms, _) = timed(other_step, args.steps)
     value = ops / (ms_per_step * 1e-3) / 1e12
     attn_tops = ops / (attn_ms * 1e-3) / 1e12
+    if args.q_path == "fused":
+        fused_ms, sep_quant_ms = main_attn_ms, other_quant_ms
+    else:
+        fused_ms, sep_quant_ms = other_attn_ms, quant_ms
 
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
@@ -393,7 +452,7 @@ def main():
 
     res = {
         "metric": METRIC, "value": round(value, 2), "unit": "TOPS", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "steps": args.steps, "warmup": args.warmup, "settle_ms": args.settle_ms, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "int8", "data": "synthetic",
         "config": {"workload": workload_desc(case), "name": args.config, "n_tokens": N,
@@ -401,8 +460,10 @@ def main():
                    "window_blocks": case.window_blocks, "sink_blocks": case.sink_blocks,
                    "attended_keys": total_keys, "int8_ops_per_step": ops, "parallelism": "single-gpu"},
         "pct_of_int8_peak_step": round(100 * value / PEAK_INT8_TOPS, 2),
-        "kernel_ms": {"quantize_q_rows": round(quant_ms, 4), "prefill_attn_i8": round(attn_ms, 4),
-                      "mask_counts": round(mask_ms, 4)},
+        "q_path": args.q_path,
+        "kernel_ms": {"prefill_attn_fused_q": round(fused_ms, 4), "quantize_q_rows": round(sep_quant_ms, 4),
+                      "prefill_attn_i8": round(attn_ms, 4), "mask_counts": round(mask_ms, 4)},
+        "other_q_path_ms_per_step": round(other_ms, 4),
         "roofline": {"bound": "mfma", "achieved": round(attn_tops, 2), "peak": PEAK_INT8_TOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tops / PEAK_INT8_TOPS, 4),
                      "traffic": traffic, "kernel": "prefill_attn_i8",

@@ -143,6 +143,28 @@ wpa_status wpa_prefill_attn_i8_chunk(const int8_t* q_i8, const float* q_scale,
                                      void* out, wpa_dtype out_dtype, hipStream_t stream);
 
 /*
+ * The attention of wpa_prefill_attn_i8_chunk straight from bf16 Q: the two
+ * attention kernels quantize each query row as they load it, with the formula
+ * of wpa_quantize_q_rows (one scale per row: int8 tensor-core prefill
+ * attention page, "Why the attention, and why tensor cores"), so the output
+ * is bitwise that of wpa_quantize_q_rows followed by
+ * wpa_prefill_attn_i8_chunk, without the int8 Q round trip through memory.
+ *   q        [n_tokens][n_q_heads][256] bf16 (q_dtype must be WPA_BF16),
+ *            16-byte aligned.  Row i is sequence position q_start + i; pass
+ *            q_start = 0 for a whole prompt.
+ * Other arguments, layouts and errors as wpa_prefill_attn_i8_chunk; a q_dtype
+ * other than WPA_BF16 -> WPA_ERR_UNSUPPORTED (float32 Q goes through
+ * wpa_quantize_q_rows).
+ */
+wpa_status wpa_prefill_attn_fused_q(const void* q, wpa_dtype q_dtype,
+                                    const int8_t* k_pool, const int8_t* v_pool,
+                                    const float* k_scale, const float* v_scale,
+                                    const int32_t* page_table, int n_pool_pages,
+                                    int q_start, int n_tokens, int n_q_heads, int n_kv_heads,
+                                    int window_blocks, int sink_blocks, float softmax_scale,
+                                    void* out, wpa_dtype out_dtype, hipStream_t stream);
+
+/*
  * counts[t] = |A(t)| for t in [0, n_tokens), computed by walking the same key
  * block list the attention kernel walks (the mask of the int8 tensor-core
  * prefill attention page, "Why the attention, and why tensor cores": window

@@ -32,6 +32,7 @@ def lib():
     L.wpa_kv_write_i8.argtypes = [vp, vp, ci, ci, ci, vp, ci, vp, vp, vp, vp, vp]
     L.wpa_prefill_attn_i8_chunk.argtypes = [vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, cf, vp, ci, vp]
     L.wpa_mask_counts_chunk.argtypes = [ci, ci, ci, ci, vp, vp]
+    L.wpa_prefill_attn_fused_q.argtypes = [vp, ci, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, cf, vp, ci, vp]
     L.wpa_decode_workspace_bytes.argtypes = [ci, ci, ci, ci, ci]
     L.wpa_decode_workspace_bytes.restype = ctypes.c_size_t
     L.wpa_decode_attn_i8.argtypes = [vp, vp, vp, vp, vp, vp, ci, vp, ci, vp, ci, ci, ci, ci, ci, cf, vp,
@@ -45,7 +46,7 @@ def test_header_declares_the_entry_points():
     fns = declared_functions()
     for f in ("wpa_quantize_q_rows", "wpa_prefill_attn_i8", "wpa_mask_counts", "wpa_kv_write_i8",
               "wpa_prefill_attn_i8_chunk", "wpa_mask_counts_chunk", "wpa_decode_attn_i8",
-              "wpa_decode_workspace_bytes", "wpa_status_string"):
+              "wpa_decode_workspace_bytes", "wpa_prefill_attn_fused_q", "wpa_status_string"):
         assert f in fns
 
 
@@ -155,6 +156,29 @@ def test_chunk_entry_points_reject_invalid_arguments(lib):
     assert m(16, -1, 4, 1, P, None) == SHAPE
     assert m(16, 10, 4, 1, None, None) == NULL
     assert m(16, 0, 4, 1, None, None) == OK
+
+
+def test_fused_q_rejects_invalid_arguments(lib):
+    def f(q=P, q_dtype=1, q_start=0, n=64, n_pool=4, **kw):
+        args = dict(k=P, v=P, ks=P, vs=P, pt=P, hq=4, hkv=2, W=0, S=0, scale=0.0625, out=P, dtype=1)
+        args.update(kw)
+        return lib.wpa_prefill_attn_fused_q(q, q_dtype, args["k"], args["v"], args["ks"], args["vs"], args["pt"],
+                                            n_pool, q_start, n, args["hq"], args["hkv"], args["W"], args["S"],
+                                            args["scale"], args["out"], args["dtype"], None)
+    assert f(q_dtype=0) == UNSUP           # float32 Q goes through wpa_quantize_q_rows
+    assert f(q_dtype=7) == UNSUP
+    assert f(n=-1) == SHAPE
+    assert f(hq=6, hkv=4) == SHAPE
+    assert f(n_pool=3) == SHAPE
+    assert f(q_start=-16) == SHAPE
+    assert f(scale=float("nan")) == SHAPE
+    assert f(q_start=8, n_pool=5) == UNSUP
+    assert f(q=ctypes.c_void_p(0x100002)) == UNSUP
+    assert f(dtype=5) == UNSUP
+    assert f(q=None) == NULL
+    assert f(out=None) == NULL
+    assert f(pt=None) == NULL
+    assert f(n=0, q=None, out=None) == OK
 
 
 def test_decode_workspace_size(lib):

@@ -13,6 +13,7 @@ Entry points mirror the C ABI in include/wpa.h:
     kv_write_i8(k, v, slots, k_pool, v_pool, k_scale, v_scale)  (writes the pools in place)
     prefill_attn_i8_chunk(q_start, q_i8, q_scale, ...same as prefill_attn_i8...) -> out
     mask_counts_chunk(q_start, n_tokens, window_blocks, sink_blocks, counts=None, device=None) -> counts
+    prefill_attn_fused_q(q, k_pool, ...same as prefill_attn_i8..., q_start=0) -> out   (bf16 Q, quantized in-kernel)
     decode_attn_i8(q_i8, q_scale, k_pool, v_pool, k_scale, v_scale, page_tables, seq_lens,
                    window_blocks, sink_blocks, softmax_scale, out=None, out_dtype=torch.bfloat16,
                    workspace=None)                     -> out
@@ -24,7 +25,8 @@ import os
 
 import torch
 
-__all__ = ["quantize_q_rows", "prefill_attn_i8", "prefill_attn_i8_chunk", "mask_counts", "mask_counts_chunk",
+__all__ = ["quantize_q_rows", "prefill_attn_i8", "prefill_attn_i8_chunk", "prefill_attn_fused_q", "mask_counts",
+           "mask_counts_chunk",
            "kv_write_i8", "decode_attn_i8", "decode_workspace_bytes", "lib", "LIB_PATH",
            "HEAD_DIM", "PAGE_TOKENS", "WpaError"]
 
@@ -54,6 +56,8 @@ def _load():
     L.wpa_prefill_attn_i8_chunk.restype = ci
     L.wpa_mask_counts_chunk.argtypes = [ci, ci, ci, ci, vp, vp]
     L.wpa_mask_counts_chunk.restype = ci
+    L.wpa_prefill_attn_fused_q.argtypes = [vp, ci, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, cf, vp, ci, vp]
+    L.wpa_prefill_attn_fused_q.restype = ci
     L.wpa_decode_workspace_bytes.argtypes = [ci, ci, ci, ci, ci]
     L.wpa_decode_workspace_bytes.restype = ctypes.c_size_t
     L.wpa_decode_attn_i8.argtypes = [vp, vp, vp, vp, vp, vp, ci, vp, ci, vp, ci, ci, ci, ci, ci, cf, vp,
@@ -128,11 +132,23 @@ def prefill_attn_i8_chunk(q_start, q_i8, q_scale, k_pool, v_pool, k_scale, v_sca
                     window_blocks, sink_blocks, softmax_scale, out, out_dtype)
 
 
+def prefill_attn_fused_q(q, k_pool, v_pool, k_scale, v_scale, page_table, window_blocks, sink_blocks,
+                         softmax_scale, out=None, out_dtype=torch.bfloat16, q_start=0):
+    """The attention of prefill_attn_i8_chunk from bf16 Q, quantized inside the attention
+    kernels (bitwise the same output as quantize_q_rows + prefill_attn_i8_chunk); see include/wpa.h."""
+    return _prefill(int(q_start), q, None, k_pool, v_pool, k_scale, v_scale, page_table,
+                    window_blocks, sink_blocks, softmax_scale, out, out_dtype, fused=True)
+
+
 def _prefill(q_start, q_i8, q_scale, k_pool, v_pool, k_scale, v_scale, page_table,
-             window_blocks, sink_blocks, softmax_scale, out, out_dtype):
-    _dev(q_i8, "q_i8", torch.int8)
+             window_blocks, sink_blocks, softmax_scale, out, out_dtype, fused=False):
+    if fused:
+        _dev(q_i8, "q", torch.bfloat16)
+    else:
+        _dev(q_i8, "q_i8", torch.int8)
     n, hq, d = q_i8.shape
-    _dev(q_scale, "q_scale", torch.float32, (n, hq))
+    if not fused:
+        _dev(q_scale, "q_scale", torch.float32, (n, hq))
     _dev(k_pool, "k_pool", torch.int8)
     n_pool, page, hkv, d2 = k_pool.shape
     if page != PAGE_TOKENS or d2 != HEAD_DIM or d != HEAD_DIM:
@@ -148,11 +164,13 @@ def _prefill(q_start, q_i8, q_scale, k_pool, v_pool, k_scale, v_scale, page_tabl
     if out.dtype not in (torch.bfloat16, torch.float32):
         raise TypeError("out must be bfloat16 or float32")
     _dev(out, "out", out.dtype, (n, hq, d))
-    common = (_ptr(q_i8), _ptr(q_scale), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale),
+    common = (_ptr(q_i8), _ptr(None if fused else q_scale), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale),
               _ptr(page_table), n_pool)
     tail = (n, hq, hkv, int(window_blocks), int(sink_blocks), float(softmax_scale), _ptr(out),
             WPA_BF16 if out.dtype == torch.bfloat16 else WPA_F32, _stream(q_i8.device))
-    if q_start is None:
+    if fused:
+        _check(lib.wpa_prefill_attn_fused_q(_ptr(q_i8), WPA_BF16, *common[2:], q_start, *tail))
+    elif q_start is None:
         _check(lib.wpa_prefill_attn_i8(*common, *tail))
     else:
         _check(lib.wpa_prefill_attn_i8_chunk(*common, q_start, *tail))

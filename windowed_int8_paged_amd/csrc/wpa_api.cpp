@@ -70,10 +70,13 @@ wpa_status wpa_kv_write_i8(const void* k, const void* v, wpa_dtype dtype, int n_
 
 namespace {
 
-wpa_status prefill_attn(const int8_t* q_i8, const float* q_scale, const int8_t* k_pool, const int8_t* v_pool,
-                        const float* k_scale, const float* v_scale, const int32_t* page_table, int n_pool_pages,
-                        int q_start, int n_tokens, int n_q_heads, int n_kv_heads, int window_blocks,
-                        int sink_blocks, float softmax_scale, void* out, wpa_dtype out_dtype, hipStream_t stream) {
+// q_bf16 == nullptr: Q comes as int8 codes and row scales; otherwise as bf16
+// and the kernels quantize it.
+wpa_status prefill_attn(const int8_t* q_i8, const float* q_scale, const uint16_t* q_bf16, const int8_t* k_pool,
+                        const int8_t* v_pool, const float* k_scale, const float* v_scale,
+                        const int32_t* page_table, int n_pool_pages, int q_start, int n_tokens, int n_q_heads,
+                        int n_kv_heads, int window_blocks, int sink_blocks, float softmax_scale, void* out,
+                        wpa_dtype out_dtype, hipStream_t stream) {
   if (n_tokens < 0 || q_start < 0 || n_q_heads <= 0 || n_kv_heads <= 0 || n_q_heads % n_kv_heads != 0)
     return WPA_ERR_SHAPE;
   if (sink_blocks < 0 || !std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return WPA_ERR_SHAPE;
@@ -82,9 +85,10 @@ wpa_status prefill_attn(const int8_t* q_i8, const float* q_scale, const int8_t* 
   if (out_dtype != WPA_BF16 && out_dtype != WPA_F32) return WPA_ERR_UNSUPPORTED;
   if (q_start % WPA_PAGE_TOKENS != 0 || seq > 0x7fffffffL - WPA_PAGE_TOKENS) return WPA_ERR_UNSUPPORTED;
   if (n_tokens == 0) return WPA_OK;
-  if (!q_i8 || !q_scale || !k_pool || !v_pool || !k_scale || !v_scale || !page_table || !out)
-    return WPA_ERR_NULL;
-  if (!aligned16(q_i8) || !aligned16(k_pool) || !aligned16(v_pool)) return WPA_ERR_UNSUPPORTED;
+  const bool have_q = q_bf16 ? true : (q_i8 && q_scale);
+  if (!have_q || !k_pool || !v_pool || !k_scale || !v_scale || !page_table || !out) return WPA_ERR_NULL;
+  if (!aligned16(q_bf16 ? (const void*)q_bf16 : (const void*)q_i8) || !aligned16(k_pool) || !aligned16(v_pool))
+    return WPA_ERR_UNSUPPORTED;
   if (max_keys_per_row(seq, window_blocks, sink_blocks) > WPA_MAX_KEYS_PER_ROW) return WPA_ERR_UNSUPPORTED;
   const long n_tiles = ceil_div(n_tokens, WPA_PAGE_TOKENS);
   if (n_tiles * n_kv_heads * ((n_q_heads / n_kv_heads + 1) / 2) > 0x7fffffffL) return WPA_ERR_UNSUPPORTED;
@@ -92,6 +96,7 @@ wpa_status prefill_attn(const int8_t* q_i8, const float* q_scale, const int8_t* 
   wpa::AttnArgs a = {};
   a.q_i8 = q_i8;
   a.q_scale = q_scale;
+  a.q_bf16 = q_bf16;
   a.k_pool = k_pool;
   a.v_pool = v_pool;
   a.k_scale = k_scale;
@@ -129,7 +134,8 @@ wpa_status wpa_prefill_attn_i8(const int8_t* q_i8, const float* q_scale, const i
                                const int32_t* page_table, int n_pool_pages, int n_tokens, int n_q_heads,
                                int n_kv_heads, int window_blocks, int sink_blocks, float softmax_scale,
                                void* out, wpa_dtype out_dtype, hipStream_t stream) {
-  return prefill_attn(q_i8, q_scale, k_pool, v_pool, k_scale, v_scale, page_table, n_pool_pages, 0, n_tokens,
+  return prefill_attn(q_i8, q_scale, nullptr, k_pool, v_pool, k_scale, v_scale, page_table, n_pool_pages, 0,
+                      n_tokens,
                       n_q_heads, n_kv_heads, window_blocks, sink_blocks, softmax_scale, out, out_dtype, stream);
 }
 
@@ -138,9 +144,21 @@ wpa_status wpa_prefill_attn_i8_chunk(const int8_t* q_i8, const float* q_scale, c
                                      const int32_t* page_table, int n_pool_pages, int q_start, int n_tokens,
                                      int n_q_heads, int n_kv_heads, int window_blocks, int sink_blocks,
                                      float softmax_scale, void* out, wpa_dtype out_dtype, hipStream_t stream) {
-  return prefill_attn(q_i8, q_scale, k_pool, v_pool, k_scale, v_scale, page_table, n_pool_pages, q_start,
-                      n_tokens, n_q_heads, n_kv_heads, window_blocks, sink_blocks, softmax_scale, out, out_dtype,
+  return prefill_attn(q_i8, q_scale, nullptr, k_pool, v_pool, k_scale, v_scale, page_table, n_pool_pages,
+                      q_start, n_tokens, n_q_heads, n_kv_heads, window_blocks, sink_blocks, softmax_scale, out, out_dtype,
                       stream);
+}
+
+wpa_status wpa_prefill_attn_fused_q(const void* q, wpa_dtype q_dtype, const int8_t* k_pool, const int8_t* v_pool,
+                                    const float* k_scale, const float* v_scale, const int32_t* page_table,
+                                    int n_pool_pages, int q_start, int n_tokens, int n_q_heads, int n_kv_heads,
+                                    int window_blocks, int sink_blocks, float softmax_scale, void* out,
+                                    wpa_dtype out_dtype, hipStream_t stream) {
+  if (q_dtype != WPA_BF16) return WPA_ERR_UNSUPPORTED;
+  // a NULL q reaches prefill_attn with no Q at all and fails its pointer check
+  return prefill_attn(nullptr, nullptr, static_cast<const uint16_t*>(q), k_pool, v_pool, k_scale, v_scale,
+                      page_table, n_pool_pages, q_start, n_tokens, n_q_heads, n_kv_heads, window_blocks, sink_blocks,
+                      softmax_scale, out, out_dtype, stream);
 }
 
 wpa_status wpa_mask_counts(int n_tokens, int window_blocks, int sink_blocks, int32_t* counts,

@@ -472,16 +472,69 @@ struct Work {
   }
   // Q codes of this lane's row for heads hd0 .. in the B-operand layout (16
   // channels per chunk) and rowf = q_scale * softmax_scale * log2(e); rows
-  // past the end read the last token and are never stored.
-  template <int H>
+  // past the end read the last token and are never stored.  With QF the
+  // lane reads the same 64 channels as bf16 and the four lanes of a row
+  // (lane, +16, +32, +48) share their maximum to quantize the row.
+  template <int H, bool QF>
   __device__ void load_q(const AttnArgs& a, int hd0, v4i (&qf)[H][4], float (&rowf)[H]) const {
     const int tq = row_ok ? my_t : a.n_tokens - 1;
 #pragma unroll
     for (int h = 0; h < H; ++h) {
-      const int8_t* qrow = a.q_i8 + ((long)tq * a.n_q_heads + hd0 + h) * kHeadDim + 16 * rc.g;
+      const long row = (long)tq * a.n_q_heads + hd0 + h;
+      if (QF) {
+        const uint4* qrow = reinterpret_cast<const uint4*>(a.q_bf16 + row * kHeadDim + 16 * rc.g);
+        uint4 raw[4][2];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) qf[h][c] = *reinterpret_cast<const v4i*>(qrow + 64 * c);
-      rowf[h] = row_ok ? a.q_scale[(long)tq * a.n_q_heads + hd0 + h] * a.row_mul : 0.f;
+        for (int c = 0; c < 4; ++c) {
+          raw[c][0] = qrow[8 * c];
+          raw[c][1] = qrow[8 * c + 1];
+        }
+        // |x| of finite values ordered as the unsigned magnitude bits; the
+        // packed words stay in registers and are widened only once, below
+        uint32_t mlo = 0, mhi = 0;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            const uint32_t w[4] = {raw[c][k].x, raw[c][k].y, raw[c][k].z, raw[c][k].w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              mlo = max(mlo, w[i] & 0x7fffu);
+              mhi = max(mhi, w[i] & 0x7fff0000u);
+            }
+          }
+        uint32_t mbits = max(mlo << 16, mhi);
+        mbits = max(mbits, (uint32_t)__shfl_xor((int)mbits, 16));
+        mbits = max(mbits, (uint32_t)__shfl_xor((int)mbits, 32));
+        const float amax = __uint_as_float(mbits);
+        const float inv = q_inv_of(amax);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          uint32_t cw[4];
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            const uint32_t w[4] = {raw[c][k].x, raw[c][k].y, raw[c][k].z, raw[c][k].w};
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+              const uint32_t lo = w[2 * i], hi = w[2 * i + 1];
+              cw[2 * k + i] = q_code(__uint_as_float(lo << 16), inv) |
+                              (q_code(__uint_as_float(lo & 0xffff0000u), inv) << 8) |
+                              (q_code(__uint_as_float(hi << 16), inv) << 16) |
+                              (q_code(__uint_as_float(hi & 0xffff0000u), inv) << 24);
+            }
+          }
+          qf[h][c] = v4i{(int)cw[0], (int)cw[1], (int)cw[2], (int)cw[3]};
+        }
+        rowf[h] = row_ok ? q_scale_of(amax) * a.row_mul : 0.f;
+        // one head's bf16 row in registers at a time (the row-max launch
+        // runs four waves per SIMD)
+        asm volatile("" ::: "memory");
+      } else {
+        const int8_t* qrow = a.q_i8 + row * kHeadDim + 16 * rc.g;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) qf[h][c] = *reinterpret_cast<const v4i*>(qrow + 64 * c);
+        rowf[h] = row_ok ? a.q_scale[row] * a.row_mul : 0.f;
+      }
     }
   }
   // First four bytes of the output row of (token t, head hd): the row-max
@@ -501,7 +554,7 @@ struct Work {
 // LDS at the end.  A step waits for its own copies, syncs (every wave is then
 // done with the other buffer), issues the next step's copies into the other
 // buffer, then computes on its own.
-template <int WPG, bool OUT_BF16>
+template <int WPG, bool OUT_BF16, bool QF>
 __global__ __launch_bounds__(64 * WPG, 4) void row_max_kernel(AttnArgs a, const int32_t* __restrict__ pt_arg) {
   constexpr int HPW = WPG >= 2 ? 2 : 1;  // query heads per wave
   constexpr int NHP = WPG / HPW;          // head groups of the workgroup
@@ -519,7 +572,7 @@ __global__ __launch_bounds__(64 * WPG, 4) void row_max_kernel(AttnArgs a, const 
   const int p0 = kh * NP;
   v4i qf[HPW][4];
   float rowf[HPW];
-  w.template load_q<HPW>(a, head0, qf, rowf);
+  w.template load_q<HPW, QF>(a, head0, qf, rowf);
   wait_vmem();
   WavePages<WPG> pg_next = wave_pages<WPG>(pt, w.tb, w.n_st > 1 ? 1 : 0, w.wave);
   float* lvs_w = lvs[w.wave];
@@ -561,7 +614,7 @@ __global__ __launch_bounds__(64 * WPG, 4) void row_max_kernel(AttnArgs a, const 
 // wave holds two heads' accumulators (256 registers) and runs alone on its
 // SIMD, every K and V fragment it reads feeding two heads; measured slower
 // than HPW = 1 at two waves per SIMD, which is what the launcher uses.
-template <int WPG, int HPW, bool OUT_BF16>
+template <int WPG, int HPW, bool OUT_BF16, bool QF>
 __global__ __launch_bounds__(64 * (WPG / HPW), HPW == 2 ? 1 : 2) void prefill_attn_kernel(
     AttnArgs a, const int32_t* __restrict__ pt_arg) {
   constexpr int NW = WPG / HPW;
@@ -571,7 +624,7 @@ __global__ __launch_bounds__(64 * (WPG / HPW), HPW == 2 ? 1 : 2) void prefill_at
   issue_stage<NW, true>(st[0], a, w.plan, w.page_bytes, w.scale_stride, wave_pages<NW>(pt, w.tb, 0, w.wave), w.wave);
   v4i qf[HPW][4];
   float rowf[HPW], neg_z[HPW], lsum[HPW];
-  w.template load_q<HPW>(a, w.head0, qf, rowf);
+  w.template load_q<HPW, QF>(a, w.head0, qf, rowf);
   // rows past the end have rowf = 0 and any finite Z; their results stay in
   // their own accumulator rows and are never stored
 #pragma unroll
@@ -630,16 +683,22 @@ __global__ __launch_bounds__(64 * (WPG / HPW), HPW == 2 ? 1 : 2) void prefill_at
   }
 }
 
-template <int WPG, int HPW, bool OUT_BF16>
+template <int WPG, int HPW, bool OUT_BF16, bool QF>
 static void launch_wpg(const AttnArgs& a, unsigned grid, hipStream_t stream) {
-  hipLaunchKernelGGL((row_max_kernel<WPG, OUT_BF16>), dim3(grid), dim3(64 * WPG), 0, stream, a, a.page_table);
-  hipLaunchKernelGGL((prefill_attn_kernel<WPG, HPW, OUT_BF16>), dim3(grid), dim3(64 * (WPG / HPW)), 0, stream, a,
-                     a.page_table);
+  hipLaunchKernelGGL((row_max_kernel<WPG, OUT_BF16, QF>), dim3(grid), dim3(64 * WPG), 0, stream, a, a.page_table);
+  hipLaunchKernelGGL((prefill_attn_kernel<WPG, HPW, OUT_BF16, QF>), dim3(grid), dim3(64 * (WPG / HPW)), 0, stream,
+                     a, a.page_table);
 }
 template <int WPG, int HPW>
 static void launch_wpg(const AttnArgs& a, bool out_bf16, unsigned grid, hipStream_t stream) {
-  if (out_bf16) launch_wpg<WPG, HPW, true>(a, grid, stream);
-  else launch_wpg<WPG, HPW, false>(a, grid, stream);
+  const bool qf = a.q_bf16 != nullptr;
+  if (out_bf16) {
+    if (qf) launch_wpg<WPG, HPW, true, true>(a, grid, stream);
+    else launch_wpg<WPG, HPW, true, false>(a, grid, stream);
+  } else {
+    if (qf) launch_wpg<WPG, HPW, false, true>(a, grid, stream);
+    else launch_wpg<WPG, HPW, false, false>(a, grid, stream);
+  }
 }
 
 hipError_t launch_prefill_attn(const AttnArgs& args_in, bool out_bf16, hipStream_t stream) {

@@ -40,4 +40,15 @@ __host__ __device__ inline TileBlocks tile_blocks(int qt, int window_blocks, int
   return tb;
 }
 
+// Per-row Q quantization (int8 tensor-core prefill attention page, "Why the
+// attention, and why tensor cores": one scale per query row).  Every kernel
+// that quantizes Q goes through these, so the separate quantize launch and the
+// attention launches that quantize their own tile give the same bits.
+__device__ inline float q_inv_of(float amax) { return amax > 0.f ? 127.0f / amax : 0.f; }
+__device__ inline float q_scale_of(float amax) { return amax > 0.f ? amax / 127.0f : 0.f; }
+__device__ inline uint32_t q_code(float v, float inv) {
+  const float c = fminf(fmaxf(rintf(v * inv), -127.f), 127.f);  // round half to even, never -128
+  return (uint32_t)(int32_t)c & 0xffu;
+}
+
 }  // namespace wpa

@@ -8,8 +8,9 @@
 namespace wpa {
 
 struct AttnArgs {
-  const int8_t* q_i8;
+  const int8_t* q_i8;       // int8 Q codes and row scales, or
   const float* q_scale;
+  const uint16_t* q_bf16;   // bf16 Q, quantized by the attention kernels themselves
   const int8_t* k_pool;
   const int8_t* v_pool;
   const float* k_scale;
@@ -56,6 +57,7 @@ hipError_t launch_kv_write(const void* k, const void* v, bool bf16, int n_tokens
                            float* v_scale, hipStream_t stream);
 hipError_t launch_mask_counts(int q_start, int n_tokens, int window_blocks, int sink_blocks, int32_t* counts,
                               hipStream_t stream);
+// q_bf16 set: the kernels quantize Q as they load it (q_i8, q_scale unused).
 hipError_t launch_prefill_attn(const AttnArgs& args, bool out_bf16, hipStream_t stream);
 
 }  // namespace wpa

@@ -41,17 +41,15 @@ __device__ inline uint2 quant8(const float (&v)[8], float& scale) {
   for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
 #pragma unroll
   for (int off = 16; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 32));
-  const float inv = amax > 0.f ? 127.0f / amax : 0.f;
+  const float inv = q_inv_of(amax);
   uint32_t lo = 0, hi = 0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    float c = rintf(v[i] * inv);
-    c = fminf(fmaxf(c, -127.f), 127.f);
-    const uint32_t b = (uint32_t)(int32_t)c & 0xffu;
+    const uint32_t b = q_code(v[i], inv);
     if (i < 4) lo |= b << (8 * i);
     else hi |= b << (8 * (i - 4));
   }
-  scale = amax > 0.f ? amax / 127.0f : 0.f;
+  scale = q_scale_of(amax);
   return make_uint2(lo, hi);
 }
 
