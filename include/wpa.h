@@ -152,9 +152,11 @@ wpa_status wpa_prefill_attn_i8_chunk(const int8_t* q_i8, const float* q_scale,
  *   q        [n_tokens][n_q_heads][256] bf16 (q_dtype must be WPA_BF16),
  *            16-byte aligned.  Row i is sequence position q_start + i; pass
  *            q_start = 0 for a whole prompt.
- * Other arguments, layouts and errors as wpa_prefill_attn_i8_chunk; a q_dtype
- * other than WPA_BF16 -> WPA_ERR_UNSUPPORTED (float32 Q goes through
- * wpa_quantize_q_rows).
+ * The first launch quantizes the rows and leaves their codes and scales in
+ * the output rows (with Z) for the second, which overwrites them; out must
+ * not alias q.  Other arguments, layouts and errors as
+ * wpa_prefill_attn_i8_chunk; a q_dtype other than WPA_BF16 ->
+ * WPA_ERR_UNSUPPORTED (float32 Q goes through wpa_quantize_q_rows).
  */
 wpa_status wpa_prefill_attn_fused_q(const void* q, wpa_dtype q_dtype,
                                     const int8_t* k_pool, const int8_t* v_pool,

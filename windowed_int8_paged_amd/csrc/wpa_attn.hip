@@ -57,6 +57,7 @@ constexpr float kCap = 1.0f + 1.0f / 4096.0f;
 constexpr float kFScale = 16777216.0f / kCap;
 constexpr uint32_t kDigitBias = (128u << 16) + (1u << 15);  // digit offset 128, rounding half
 constexpr float kTiny = 0x1p-60f;
+constexpr int kQCodeOffset = 256;  // byte offset of the handed-over Q codes in an output row
 
 // One stage buffer.  K and V tiles are row-major (row = key of the step, 256
 // bytes) with the 16-byte chunk c of row r stored in slot c ^ swz(r).  The
@@ -434,6 +435,12 @@ __device__ inline void pass2_step(const Stage& st, const v4i (&qf)[HPW][4], int 
   }
 }
 
+// Where a launch finds its Q rows: int8 codes and row scales from the
+// caller; bf16 from the caller, quantized on load; or (attention launch of
+// the fused path) the codes and scale the row-max launch left in the row's
+// output slot.
+enum class QSrc { kInt8, kBf16, kOutRow };
+
 // What a wave knows about its work item: workgroup u covers query tile qt
 // (absolute: the call's rows start at tile a.tile0 of the sequence), KV head
 // kvh and NW*HPW of its query heads; wave w takes heads head0 .. head0+HPW-1
@@ -472,16 +479,16 @@ struct Work {
   }
   // Q codes of this lane's row for heads hd0 .. in the B-operand layout (16
   // channels per chunk) and rowf = q_scale * softmax_scale * log2(e); rows
-  // past the end read the last token and are never stored.  With QF the
-  // lane reads the same 64 channels as bf16 and the four lanes of a row
-  // (lane, +16, +32, +48) share their maximum to quantize the row.
-  template <int H, bool QF>
-  __device__ void load_q(const AttnArgs& a, int hd0, v4i (&qf)[H][4], float (&rowf)[H]) const {
+  // past the end read the last token and are never stored.  From bf16 the
+  // lane reads the same 64 channels and the four lanes of a row (lane, +16,
+  // +32, +48) share their maximum to quantize the row.
+  template <int H, QSrc QS, bool OUT_BF16>
+  __device__ void load_q(const AttnArgs& a, int hd0, v4i (&qf)[H][4], float (&rowf)[H], float (&qscale)[H]) const {
     const int tq = row_ok ? my_t : a.n_tokens - 1;
 #pragma unroll
     for (int h = 0; h < H; ++h) {
       const long row = (long)tq * a.n_q_heads + hd0 + h;
-      if (QF) {
+      if (QS == QSrc::kBf16) {
         const uint4* qrow = reinterpret_cast<const uint4*>(a.q_bf16 + row * kHeadDim + 16 * rc.g);
         uint4 raw[4][2];
 #pragma unroll
@@ -517,32 +524,43 @@ struct Work {
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
               const uint32_t lo = w[2 * i], hi = w[2 * i + 1];
-              cw[2 * k + i] = q_code(__uint_as_float(lo << 16), inv) |
-                              (q_code(__uint_as_float(lo & 0xffff0000u), inv) << 8) |
-                              (q_code(__uint_as_float(hi << 16), inv) << 16) |
-                              (q_code(__uint_as_float(hi & 0xffff0000u), inv) << 24);
+              cw[2 * k + i] = q_code4(__uint_as_float(lo << 16), __uint_as_float(lo & 0xffff0000u),
+                                      __uint_as_float(hi << 16), __uint_as_float(hi & 0xffff0000u), inv);
             }
           }
           qf[h][c] = v4i{(int)cw[0], (int)cw[1], (int)cw[2], (int)cw[3]};
         }
-        rowf[h] = row_ok ? q_scale_of(amax) * a.row_mul : 0.f;
+        qscale[h] = q_scale_of(amax);
+        rowf[h] = row_ok ? qscale[h] * a.row_mul : 0.f;
         // one head's bf16 row in registers at a time (the row-max launch
         // runs four waves per SIMD)
         asm volatile("" ::: "memory");
+      } else if (QS == QSrc::kOutRow) {
+        const int8_t* slot = out_row_t<OUT_BF16>(a, tq, hd0 + h);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) qf[h][c] = *reinterpret_cast<const v4i*>(slot + kQCodeOffset + 64 * c + 16 * rc.g);
+        qscale[h] = reinterpret_cast<const float*>(slot)[1];
+        rowf[h] = row_ok ? qscale[h] * a.row_mul : 0.f;
       } else {
         const int8_t* qrow = a.q_i8 + row * kHeadDim + 16 * rc.g;
 #pragma unroll
         for (int c = 0; c < 4; ++c) qf[h][c] = *reinterpret_cast<const v4i*>(qrow + 64 * c);
-        rowf[h] = row_ok ? a.q_scale[row] * a.row_mul : 0.f;
+        qscale[h] = a.q_scale[row];
+        rowf[h] = row_ok ? qscale[h] * a.row_mul : 0.f;
       }
     }
   }
-  // First four bytes of the output row of (token t, head hd): the row-max
-  // launch leaves Z there and the attention launch overwrites it.
-  __device__ float* z_slot(const AttnArgs& a, int t, int hd, bool bf16) const {
+  // The output row of (token t, head hd) as bytes.  Between the launches it
+  // carries the row-max launch's results: Z in bytes 0-3 and, on the fused
+  // path, the Q row scale in bytes 4-7 and the 256 Q codes from byte 256.
+  // The attention launch reads them and then overwrites the row.
+  template <bool OUT_BF16>
+  __device__ int8_t* out_row_t(const AttnArgs& a, int t, int hd) const {
     const long e = ((long)t * a.n_q_heads + hd) * kHeadDim;
-    return bf16 ? reinterpret_cast<float*>(reinterpret_cast<uint16_t*>(a.out) + e)
-                : reinterpret_cast<float*>(a.out) + e;
+    return reinterpret_cast<int8_t*>(a.out) + e * (OUT_BF16 ? 2 : 4);
+  }
+  __device__ float* z_slot(const AttnArgs& a, int t, int hd, bool bf16) const {
+    return reinterpret_cast<float*>(bf16 ? out_row_t<true>(a, t, hd) : out_row_t<false>(a, t, hd));
   }
 };
 
@@ -572,7 +590,18 @@ __global__ __launch_bounds__(64 * WPG, 4) void row_max_kernel(AttnArgs a, const 
   const int p0 = kh * NP;
   v4i qf[HPW][4];
   float rowf[HPW];
-  w.template load_q<HPW, QF>(a, head0, qf, rowf);
+  float qscale[HPW];
+  w.template load_q<HPW, QF ? QSrc::kBf16 : QSrc::kInt8, OUT_BF16>(a, head0, qf, rowf, qscale);
+  if (QF && kh == 0 && w.row_ok) {
+    // hand the codes and the row scale to the attention launch
+#pragma unroll
+    for (int h = 0; h < HPW; ++h) {
+      int8_t* slot = w.template out_row_t<OUT_BF16>(a, w.my_t, head0 + h);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) *reinterpret_cast<v4i*>(slot + kQCodeOffset + 64 * c + 16 * w.rc.g) = qf[h][c];
+      if (w.rc.g == 0) reinterpret_cast<float*>(slot)[1] = qscale[h];
+    }
+  }
   wait_vmem();
   WavePages<WPG> pg_next = wave_pages<WPG>(pt, w.tb, w.n_st > 1 ? 1 : 0, w.wave);
   float* lvs_w = lvs[w.wave];
@@ -624,7 +653,8 @@ __global__ __launch_bounds__(64 * (WPG / HPW), HPW == 2 ? 1 : 2) void prefill_at
   issue_stage<NW, true>(st[0], a, w.plan, w.page_bytes, w.scale_stride, wave_pages<NW>(pt, w.tb, 0, w.wave), w.wave);
   v4i qf[HPW][4];
   float rowf[HPW], neg_z[HPW], lsum[HPW];
-  w.template load_q<HPW, QF>(a, w.head0, qf, rowf);
+  float qscale[HPW];
+  w.template load_q<HPW, QF ? QSrc::kOutRow : QSrc::kInt8, OUT_BF16>(a, w.head0, qf, rowf, qscale);
   // rows past the end have rowf = 0 and any finite Z; their results stay in
   // their own accumulator rows and are never stored
 #pragma unroll

@@ -46,9 +46,20 @@ __host__ __device__ inline TileBlocks tile_blocks(int qt, int window_blocks, int
 // attention launches that quantize their own tile give the same bits.
 __device__ inline float q_inv_of(float amax) { return amax > 0.f ? 127.0f / amax : 0.f; }
 __device__ inline float q_scale_of(float amax) { return amax > 0.f ? amax / 127.0f : 0.f; }
-__device__ inline uint32_t q_code(float v, float inv) {
-  const float c = fminf(fmaxf(rintf(v * inv), -127.f), 127.f);  // round half to even, never -128
-  return (uint32_t)(int32_t)c & 0xffu;
+// Four codes rint(v * inv), little-endian in one word.  The product is
+// rounded to float first, as the definition states; adding 1.5 * 2^23 then
+// rounds it half-to-even to an integer held in the low mantissa bits, whose
+// low byte is the code in two's complement.  No clamp is needed: |v| <= amax
+// gives |v * inv| <= 127 * (1 + 2^-23) < 127.5 for finite rows, so the code
+// is never -128 and never above 127.
+__device__ inline uint32_t q_code4(float v0, float v1, float v2, float v3, float inv) {
+#pragma clang fp contract(off)
+  constexpr float kRound = 12582912.0f;
+  const uint32_t b0 = __float_as_uint(v0 * inv + kRound), b1 = __float_as_uint(v1 * inv + kRound);
+  const uint32_t b2 = __float_as_uint(v2 * inv + kRound), b3 = __float_as_uint(v3 * inv + kRound);
+  const uint32_t lo = __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u);  // bytes: b0.0, b1.0, 0, 0
+  const uint32_t hi = __builtin_amdgcn_perm(b3, b2, 0x0c0c0400u);
+  return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
 }
 
 }  // namespace wpa

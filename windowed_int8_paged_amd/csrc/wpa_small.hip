@@ -42,15 +42,8 @@ __device__ inline uint2 quant8(const float (&v)[8], float& scale) {
 #pragma unroll
   for (int off = 16; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 32));
   const float inv = q_inv_of(amax);
-  uint32_t lo = 0, hi = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t b = q_code(v[i], inv);
-    if (i < 4) lo |= b << (8 * i);
-    else hi |= b << (8 * (i - 4));
-  }
   scale = q_scale_of(amax);
-  return make_uint2(lo, hi);
+  return make_uint2(q_code4(v[0], v[1], v[2], v[3], inv), q_code4(v[4], v[5], v[6], v[7], inv));
 }
 
 template <bool BF16>
