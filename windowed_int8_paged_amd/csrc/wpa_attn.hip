@@ -18,8 +18,9 @@
 //   * One workgroup = one 16-token query tile x one KV head x up to 4 of its
 //     query heads.  In the attention launch a wave takes one head (16 query
 //     rows) and needs at most 256 registers, so two waves share each SIMD; in
-//     the row-max launch a wave takes two heads and half of the keys, so each
-//     K fragment read from LDS feeds two products, and four waves share a SIMD.
+//     the row-max launch a wave takes all four heads and one page of each
+//     step, so each K fragment read from LDS feeds four products, and four
+//     waves share a SIMD.
 //   * Scores are computed transposed, S^T = K . Q^T, with
 //     v_mfma_i32_16x16x64_i8 per 16-key page: a lane holds 4 keys of one query
 //     row per page, so row reductions are in-lane plus lane swaps.
@@ -220,32 +221,13 @@ __device__ inline uint32_t key_mask(const TileBlocks& tb, int step, const RowCtx
   return m;
 }
 
-// S^T = K . Q^T for HPW query heads and NP pages (p0 ..) of a step: K
+// S^T = K . Q^T for HPW query heads and NP pages (p0 ..) of a step: each K
 // fragment (16 keys x 64 channels, one ds_read_b128) feeds HPW products.
 // Afterwards s[h][pp] register i of lane l holds query row l%16 and key
-// 4(l/16) + i of page p0 + pp.
-template <int HPW, int NP>
-__device__ inline void qk_pages(const int8_t* kb, const v4i (&qf)[HPW][4], int p0, int lane, v4i (&s)[HPW][NP]) {
-  const int g = lane >> 4;
-#pragma unroll
-  for (int pp = 0; pp < NP; ++pp) {
-    const int r = 16 * (p0 + pp) + (lane & 15);
-#pragma unroll
-    for (int h = 0; h < HPW; ++h) s[h][pp] = v4i{0, 0, 0, 0};
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int slot = (4 * c + g) ^ swz(r);
-      const v4i kf = *reinterpret_cast<const v4i*>(kb + r * kHeadDim + 16 * slot);
-#pragma unroll
-      for (int h = 0; h < HPW; ++h) s[h][pp] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kf, qf[h][c], s[h][pp], 0, 0, 0);
-    }
-  }
-}
-
-// The same with the fragment reads software-pipelined D fragments ahead of
-// their products.  The scheduling fences keep the compiler from sinking the
-// reads back next to their uses (it would otherwise reuse one register set
-// and wait out the full LDS latency before every product).
+// 4(l/16) + i of page p0 + pp.  The fragment reads are software-pipelined D
+// fragments ahead of their products; the scheduling fences keep the compiler
+// from sinking them back next to their uses (it would otherwise reuse one
+// register set and wait out the full LDS latency before every product).
 template <int HPW, int NP, int D>
 __device__ inline void qk_pages_pipelined(const int8_t* kb, const v4i (&qf)[HPW][4], int p0, int lane,
                                           v4i (&s)[HPW][NP]) {
@@ -284,7 +266,7 @@ __device__ inline void rowmax_step(const S& st, float* lvs_w, const v4i (&qf)[HP
                                    const float (&rowf)[HPW], uint32_t kmask, float (&zmax)[HPW]) {
   lvs_w[lane] = __builtin_amdgcn_logf(st.sc[p0 + ((lane >> 4) & (NP - 1))][16 + (lane & 15)]);
   v4i s[HPW][NP];
-  qk_pages<HPW, NP>(st.k, qf, p0, lane, s);
+  qk_pages_pipelined<HPW, NP, 4>(st.k, qf, p0, lane, s);
   __builtin_amdgcn_wave_barrier();
 #pragma unroll
   for (int pp = 0; pp < NP; ++pp) {
@@ -566,41 +548,60 @@ struct Work {
 
 // First launch, pass 1: the row maximum Z of z over the tile's key list for
 // every (query row, head).  It stages only K and the scales and needs few
-// registers, so four waves share each SIMD.  A wave takes HPW of the
-// workgroup's WPG query heads and 4/KS pages of each step (K fragments read
-// once serve HPW heads); the KS partial maxima of a row are combined through
-// LDS at the end.  A step waits for its own copies, syncs (every wave is then
-// done with the other buffer), issues the next step's copies into the other
-// buffer, then computes on its own.
+// registers, so four waves share each SIMD.  Every wave takes all WPG query
+// heads of the workgroup and page w*NP .. of each step (a K fragment read
+// once serves WPG products); the WPG partial maxima of a row are combined
+// through LDS at the end.  A step waits for its own copies, syncs (every wave
+// is then done with the other buffer), issues the next step's copies into the
+// other buffer, then computes on its own.
+//
+// From bf16 Q (QF) wave w quantizes head w only, hands the codes and scale to
+// the attention launch through the row's output slot, and shares them with
+// the other waves through the second stage buffer, which no copy has
+// targeted yet.
 template <int WPG, bool OUT_BF16, bool QF>
 __global__ __launch_bounds__(64 * WPG, 4) void row_max_kernel(AttnArgs a, const int32_t* __restrict__ pt_arg) {
-  constexpr int HPW = WPG >= 2 ? 2 : 1;  // query heads per wave
-  constexpr int NHP = WPG / HPW;          // head groups of the workgroup
-  constexpr int KS = WPG / NHP;           // key splits
-  constexpr int NP = 4 / KS;              // pages of a step per wave
+  constexpr int HPW = WPG;    // query heads per wave
+  constexpr int KS = WPG;     // key splits: one per wave
+  constexpr int NP = 4 / KS;  // pages of a step per wave
   __shared__ StageK st[2];
   __shared__ alignas(16) float lvs[WPG][kStepKeys];  // per-wave log2(v_scale) of its pages
   __shared__ float zpart[KS][WPG][16];
+  __shared__ float qs_lds[WPG][16];
   const WPA_CONST int32_t* pt = (const WPA_CONST int32_t*)pt_arg;
-  Work<WPG, 1> w(a);  // one wave per head for the copies; heads are regrouped below
+  Work<WPG, 1> w(a);  // w.head0 is this wave's own head
   issue_stage<WPG, false>(st[0], a, w.plan, w.page_bytes, w.scale_stride, wave_pages<WPG>(pt, w.tb, 0, w.wave), w.wave);
 
-  const int hp = w.wave % NHP, kh = w.wave / NHP;
-  const int head0 = w.head0 - w.wave + hp * HPW;  // first head of this wave
+  const int kh = w.wave;
+  const int head0 = w.head0 - w.wave;  // the workgroup's first head
   const int p0 = kh * NP;
   v4i qf[HPW][4];
   float rowf[HPW];
-  float qscale[HPW];
-  w.template load_q<HPW, QF ? QSrc::kBf16 : QSrc::kInt8, OUT_BF16>(a, head0, qf, rowf, qscale);
-  if (QF && kh == 0 && w.row_ok) {
-    // hand the codes and the row scale to the attention launch
+  if (QF) {
+    v4i own[1][4];
+    float own_rowf[1], own_scale[1];
+    w.template load_q<1, QSrc::kBf16, OUT_BF16>(a, w.head0, own, own_rowf, own_scale);
+    int8_t* share = st[1].k + (w.wave * kPage + (w.lane & 15)) * kHeadDim + 16 * w.rc.g;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) *reinterpret_cast<v4i*>(share + 64 * c) = own[0][c];
+    if (w.rc.g == 0) qs_lds[w.wave][w.lane] = own_scale[0];
+    if (w.row_ok) {  // hand the codes and the row scale to the attention launch
+      int8_t* slot = w.template out_row_t<OUT_BF16>(a, w.my_t, w.head0);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) *reinterpret_cast<v4i*>(slot + kQCodeOffset + 64 * c + 16 * w.rc.g) = own[0][c];
+      if (w.rc.g == 0) reinterpret_cast<float*>(slot)[1] = own_scale[0];
+    }
+    __syncthreads();
 #pragma unroll
     for (int h = 0; h < HPW; ++h) {
-      int8_t* slot = w.template out_row_t<OUT_BF16>(a, w.my_t, head0 + h);
+      const int8_t* src = st[1].k + (h * kPage + (w.lane & 15)) * kHeadDim + 16 * w.rc.g;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) *reinterpret_cast<v4i*>(slot + kQCodeOffset + 64 * c + 16 * w.rc.g) = qf[h][c];
-      if (w.rc.g == 0) reinterpret_cast<float*>(slot)[1] = qscale[h];
+      for (int c = 0; c < 4; ++c) qf[h][c] = *reinterpret_cast<const v4i*>(src + 64 * c);
+      rowf[h] = w.row_ok ? qs_lds[h][w.lane & 15] * a.row_mul : 0.f;
     }
+  } else {
+    float qscale[HPW];
+    w.template load_q<HPW, QSrc::kInt8, OUT_BF16>(a, head0, qf, rowf, qscale);
   }
   wait_vmem();
   WavePages<WPG> pg_next = wave_pages<WPG>(pt, w.tb, w.n_st > 1 ? 1 : 0, w.wave);
@@ -624,15 +625,15 @@ __global__ __launch_bounds__(64 * WPG, 4) void row_max_kernel(AttnArgs a, const 
 #pragma unroll
   for (int h = 0; h < HPW; ++h) {
     const float z = rows_max(zmax[h]);
-    if (w.rc.g == 0) zpart[kh][hp * HPW + h][w.lane] = z;
+    if (w.rc.g == 0) zpart[kh][h][w.lane] = z;
   }
   __syncthreads();
   if (kh == 0 && w.rc.g == 0 && w.row_ok) {
 #pragma unroll
     for (int h = 0; h < HPW; ++h) {
-      float z = zpart[0][hp * HPW + h][w.lane];
+      float z = zpart[0][h][w.lane];
 #pragma unroll
-      for (int k = 1; k < KS; ++k) z = fmaxf(z, zpart[k][hp * HPW + h][w.lane]);
+      for (int k = 1; k < KS; ++k) z = fmaxf(z, zpart[k][h][w.lane]);
       *w.z_slot(a, w.my_t, head0 + h, OUT_BF16) = z;
     }
   }
