@@ -25,7 +25,8 @@ sys.path.insert(0, ROOT)
 METRIC = "int8 TOPS & % of MI355X int8 MFMA peak, hd256 windowed prefill attn at 32k"
 PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 matrix peak, 5.0 POP/s
 HBM_PEAK_GBS = 8000.0
-ATTN_KERNEL_SOURCES = ["windowed_int8_paged_amd/csrc/wpa_attn.hip", "windowed_int8_paged_amd/csrc/wpa_common.h"]
+ATTN_KERNEL_SOURCES = ["windowed_int8_paged_amd/csrc/wpa_attn.hip", "windowed_int8_paged_amd/csrc/wpa_common.h",
+                       "windowed_int8_paged_amd/csrc/wpa_lanes.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_prefill_attn_32k.json")
 
 

@@ -36,14 +36,10 @@
 //     V operands are gathered with the transposing read ds_read_b64_tr_b8.
 
 #include "wpa_common.h"
+#include "wpa_lanes.h"
 #include "wpa_launch.h"
 
 namespace wpa {
-
-typedef int v2i __attribute__((ext_vector_type(2)));
-typedef int v4i __attribute__((ext_vector_type(4)));
-#define WPA_LDS __attribute__((address_space(3)))
-#define WPA_CONST __attribute__((address_space(4)))
 
 constexpr int kStepKeys = 64;                 // keys per step (four pages)
 constexpr int kStage = kStepKeys * kHeadDim;  // bytes of one staged K or V tile
@@ -60,12 +56,6 @@ constexpr uint32_t kDigitBias = (128u << 16) + (1u << 15);  // digit offset 128,
 constexpr float kTiny = 0x1p-60f;
 constexpr int kQCodeOffset = 256;  // byte offset of the handed-over Q codes in an output row
 
-// One stage buffer.  K and V tiles are row-major (row = key of the step, 256
-// bytes) with the 16-byte chunk c of row r stored in slot c ^ swz(r).  The
-// operand reads below then touch every bank once per half wave: the K reads
-// see 16 consecutive rows of one page (slots r%16 ^ const), the transposing V
-// reads rows 8h..8h+7 and 16+8h..16+8h+7 (slots m and 8 + m).
-__device__ inline int swz(int r) { return (r & 15) ^ (((r >> 4) & 1) << 3); }
 // Scales of page p of the step: sc[p][0..15] k_scale, sc[p][16..31] v_scale
 // of its 16 keys (one 256-byte copy per page; slots 32..63 repeat them).
 struct alignas(16) Stage {
@@ -77,35 +67,6 @@ struct alignas(16) StageK {  // the row-max launch stages no V
   int8_t k[kStage];
   float sc[4][64];
 };
-
-// ---- cross-lane helpers: rows of 16 lanes R0..R3
-__device__ inline void swap16(float& a, float& b) {  // a <-> odd rows of b, as one instruction
-  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-  a = __uint_as_float(r[0]);
-  b = __uint_as_float(r[1]);
-}
-__device__ inline void swap32(float& a, float& b) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-  a = __uint_as_float(r[0]);
-  b = __uint_as_float(r[1]);
-}
-// all-reduce over the four 16-lane rows (same query row, different keys)
-__device__ inline float rows_max(float x) {
-  float y = x;
-  swap16(x, y);
-  x = fmaxf(x, y);
-  y = x;
-  swap32(x, y);
-  return fmaxf(x, y);
-}
-__device__ inline float rows_sum(float x) {
-  float y = x;
-  swap16(x, y);
-  x = x + y;
-  y = x;
-  swap32(x, y);
-  return x + y;
-}
 
 // Each wave copies 4/WPG whole pages of a step: list entries
 // 4s + wave*PPW + i.  Their physical pages are read through the scalar cache
@@ -287,41 +248,6 @@ __device__ inline void rowmax_step(const S& st, float* lvs_w, const v4i (&qf)[HP
   __builtin_amdgcn_wave_barrier();
 }
 
-// Page maxima over the four 16-lane rows for the four pages at once:
-// afterwards every lane holds all four.  The values are the bit patterns of
-// non-negative floats, whose unsigned order is their float order, so the
-// maxima are integer maxima (no NaN-quieting canonicalisations).
-__device__ inline uint32_t swap16u(uint32_t& a, uint32_t& b) {
-  auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
-  a = r[0];
-  b = r[1];
-  return a;
-}
-__device__ inline void swap32u(uint32_t& a, uint32_t& b) {
-  auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
-  a = r[0];
-  b = r[1];
-}
-__device__ inline void page_maxima(uint32_t (&mx)[4]) {
-  uint32_t a = mx[0], b = mx[1], c = mx[2], d = mx[3];
-  swap16u(a, b);
-  const uint32_t x01 = max(a, b);  // R0: p0(R0,R1)  R1: p1(R0,R1)  R2: p0(R2,R3)  R3: p1(R2,R3)
-  swap16u(c, d);
-  const uint32_t x23 = max(c, d);
-  uint32_t e0 = x01, e1 = x23;
-  swap32u(e0, e1);
-  const uint32_t y = max(e0, e1);  // row Rk holds the full max of page k
-  uint32_t g0 = y, g1 = y;
-  swap16u(g0, g1);  // rows 0,1: (M0, M1); rows 2,3: (M2, M3)
-  uint32_t m0 = g0, m2 = g0, m1 = g1, m3 = g1;
-  swap32u(m0, m2);  // every lane: m0 = M0, m2 = M2
-  swap32u(m1, m3);
-  mx[0] = m0;
-  mx[1] = m1;
-  mx[2] = m2;
-  mx[3] = m3;
-}
-
 // Pass 2, one step for HPW heads: e = exp2(z - Z - log2 v_scale) = P, l += P,
 // P' = P * v_scale <= 1, per-page codes code = rint(P' * 127 / max P'), their
 // weights ps * code as the fixed-point integer x = rint(code * f),
@@ -381,23 +307,10 @@ __device__ inline void pass2_step(const Stage& st, const v4i (&qf)[HPW][4], int 
     }
   }
 
-  // V operand: lane (row g, column j) needs 16 keys of channel 16nt + j in the
-  // slot order of P: slot b holds key 16(b/4) + 4g + b%4.  Two transposing
-  // reads give slots 0-7 (pages 0, 1) and 8-15 (pages 2, 3).
-  const int j = lane & 15;
-  const int kk = j >> 1;
-  const int key1 = 16 * (kk >> 2) + 4 * g + (kk & 3);
-  const int8_t* row1 = st.v + key1 * kHeadDim + 8 * (j & 1);
-  const int8_t* row2 = row1 + 32 * kHeadDim;  // key1 + 32
-  const int sw = swz(key1);
-  const int sw2 = swz(key1 + 32);
-  // reads run two column tiles ahead of their products (see qk_pages_pipelined)
+  // V operand (see VFrag): reads run two column tiles ahead of their products
+  // (see qk_pages_pipelined)
   constexpr int DV = 2;
-  auto read_v = [&](int nt) {
-    const v2i lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32((WPA_LDS v2i*)(row1 + 16 * (nt ^ sw)));
-    const v2i hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32((WPA_LDS v2i*)(row2 + 16 * (nt ^ sw2)));
-    return v4i{lo.x, lo.y, hi.x, hi.y};
-  };
+  const VFrag read_v(st.v, lane);
   v4i vf[16];
 #pragma unroll
   for (int nt = 0; nt < DV; ++nt) {

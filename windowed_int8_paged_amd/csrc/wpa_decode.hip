@@ -12,49 +12,57 @@
 // full causal attention).
 //
 // Design
-//   * A workgroup takes one (sequence, KV head, split): the G query heads of
-//     the KV head share every K and V row it loads.  A split is 8 pages (128
+//   * A workgroup takes one (sequence, KV head, split): the G <= 16 query heads
+//     of the KV head share every K and V row it loads.  A split is 8 pages (128
 //     keys) of the sequence's key list, so short batches still spread over
 //     the chip; a second launch combines the splits.
 //   * The P codes of a block depend only on the ratios of P*v_scale inside the
 //     block, so each split can use its own maximum Z_s: it returns
 //     O_s = sum_blocks ps * (codes . v) and l_s = sum P, both relative to
 //     2^Z_s, and the combine weighs split s by 2^(Z_s - max Z).  The per-block
-//     step ps is applied in float after each block's int32 sum, as the method
-//     writes it; decode is bound by HBM, not by this vector work.
-//   * QK^T uses v_dot4_i32_i8 on K rows read straight from the pool; V is
-//     staged in LDS (16-byte chunks XOR-swizzled by key) for the PV reads.
+//     step ps is applied in float to each block's int32 sum, as the method
+//     writes it.
+//   * Every load of a split is issued before any is waited on: page ids by
+//     scalar loads, then Q and K straight into matrix-operand registers, V rows
+//     and the scales.  QK^T runs on v_mfma_i32_16x16x64_i8 as S^T = K . Q^T
+//     (wave w takes pages 2w, 2w+1 of the split; a lane then holds one head
+//     and four keys per page).  PV runs on the same instruction with a block-diagonal P
+//     operand: its 16 rows are (head, page) pairs, row (h, p) holding head
+//     h's codes for the keys of page p and zeros elsewhere, so one product
+//     over 64 keys returns the int32 sum of each page separately; wave w takes
+//     16-channel tiles 4w .. 4w+3.  V is staged in LDS in the attention
+//     kernel's swizzled 64-key tiles and read with the same transposing reads.
 
 #include "wpa_common.h"
+#include "wpa_lanes.h"
 #include "wpa_launch.h"
 
 namespace wpa {
 
-constexpr int kSplitPages = 8;
-constexpr int kSplitKeys = kSplitPages * kPage;  // 128
+constexpr int kSplitPages = 8;  // 4 and 16 measured no faster
+constexpr int kSplitKeys = kSplitPages * kPage;
+constexpr int kPPW = kSplitPages / 4;  // pages per wave in QK^T and the softmax
+constexpr int kTileKeys = 64;                    // keys of one PV product (four pages)
 constexpr float kLog2eD = 1.4426950408889634f;
 
-__device__ inline int dswz(int r) { return r & 15; }  // chunk slot XOR of key r
-
 __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
-  __shared__ alignas(16) int8_t q_lds[kMaxDecodeG][kHeadDim];
-  __shared__ alignas(16) int8_t v_lds[kSplitKeys][kHeadDim];
-  __shared__ float rowf_lds[kMaxDecodeG];
-  __shared__ float ks_lds[kSplitKeys], lv_lds[kSplitKeys], vs_lds[kSplitKeys];
-  __shared__ float s_lds[kMaxDecodeG][kSplitKeys];  // acc * k_scale; -inf for masked keys
-  __shared__ int8_t code_lds[kMaxDecodeG][kSplitKeys];
+  __shared__ alignas(16) int8_t v_lds[kSplitKeys / kTileKeys][kTileKeys * kHeadDim];
+  __shared__ uint32_t code_lds[kMaxDecodeG][kSplitKeys / 4];  // four codes per word, keys 4m .. 4m+3
   __shared__ float ps_lds[kMaxDecodeG][kSplitPages];
-  __shared__ float z_lds[kMaxDecodeG], l_lds[kMaxDecodeG];
-  __shared__ int page_lds[kSplitPages], pos_lds[kSplitPages];
+  __shared__ float zpart[4][16], lpart[4][16];
+  __shared__ float ks_lds[kSplitKeys], vs_lds[kSplitKeys], lv_lds[kSplitKeys];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, n = lane & 15;
   int u = blockIdx.x;
   const int sp = u % a.n_splits;
   u /= a.n_splits;
   const int kvh = u % a.n_kv_heads;
   const int b = u / a.n_kv_heads;
   const int G = a.G;
-  float* ws = a.ws + ((long)b * a.n_q_heads + (long)kvh * G) * a.n_splits * kWsRow;
+  const long head_row0 = (long)b * a.n_q_heads + (long)kvh * G;  // Q / ws row of head 0 of this KV head
+  float* ws = a.ws + head_row0 * a.n_splits * kWsRow;
 
   // the query position; lengths beyond the page table are clamped to it
   const int len = min(a.seq_lens[b], kPage * a.max_blocks);
@@ -62,208 +70,236 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   const TileBlocks tb = tile_blocks(t >= 0 ? t / kPage : 0, a.window_blocks, a.sink_blocks);
   const int first = sp * kSplitPages;
   const int nb = t < 0 ? 0 : min(kSplitPages, tb.n_total - first);
-  if (nb <= 0) {  // nothing to attend in this split
-    if (tid < G) {
-      float* w = ws + ((long)tid * a.n_splits + sp) * kWsRow;
-      w[kHeadDim] = -INFINITY;
-      w[kHeadDim + 1] = 0.f;
+  if (nb <= 0) {  // nothing to attend in this split: O = 0, Z = -inf, l = 0
+    for (int h = 0; h < G; ++h) {
+      float* w = ws + ((long)h * a.n_splits + sp) * kWsRow;
+      w[tid] = 0.f;
+      if (tid == 0) {
+        w[kHeadDim] = -INFINITY;
+        w[kHeadDim + 1] = 0.f;
+      }
     }
     return;
   }
 
-  // ---- stage: page ids first, then every global load of the split is issued
-  // before anything waits on one (Q rows, V rows, K rows, scales)
-  if (tid < kSplitPages) {
-    const int blk = tb.block(min(first + tid, tb.n_total - 1));
-    const int pg = a.page_tables[(long)b * a.max_blocks + blk];
-    page_lds[tid] = min(max(pg, 0), a.n_pool_pages - 1);  // a bad entry reads a wrong page, never out of bounds
-    pos_lds[tid] = kPage * blk;
-  }
-  __syncthreads();
-  const int r16 = tid >> 4, c16 = tid & 15;  // staging: key r16 of each page, 16-byte chunk c16
-  const int j = tid >> 1, half = tid & 1;     // scores: key j of the split, half of the channels
-  uint4 qv, vv[kSplitPages];
-  int4 kr[8];
-  float ksv = 0.f, vsv = 0.f;
-  if (r16 < G) qv = *reinterpret_cast<const uint4*>(a.q_i8 + ((long)b * a.n_q_heads + kvh * G + r16) * kHeadDim +
-                                                    16 * c16);
-  // Straight-line loads: slots past the split's last page repeat a page of the
-  // split (page_lds clamps), so every load is in bounds and none waits on a
-  // branch; what they bring is masked or never read.
+  // ---- page ids (scalar loads; slots past the split's last page repeat it,
+  // and a bad entry is clamped into the pool: a wrong page, never out of bounds)
+  const WPA_CONST int32_t* pt = (const WPA_CONST int32_t*)a.page_tables + (long)b * a.max_blocks;
+  int page[kSplitPages], pos[kSplitPages];
 #pragma unroll
   for (int p = 0; p < kSplitPages; ++p) {
-    const long row = ((long)page_lds[p] * kPage + r16) * a.n_kv_heads + kvh;
+    const int blk = tb.block(min(first + p, tb.n_total - 1));
+    page[p] = min(max(pt[blk], 0), a.n_pool_pages - 1);
+    pos[p] = kPage * blk;
+  }
+
+  // ---- every load of the split
+  const int hq = min(n, G - 1);  // lanes of heads past G repeat the last head; never stored
+  v4i qf[4], kf[kPPW][4];
+  {
+    const int8_t* qrow = a.q_i8 + (head_row0 + hq) * kHeadDim + 16 * g;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) qf[c] = *reinterpret_cast<const v4i*>(qrow + 64 * c);
+  }
+  const float rowf = a.q_scale[head_row0 + hq] * a.row_mul;
+#pragma unroll
+  for (int pp = 0; pp < kPPW; ++pp) {
+    const long row = ((long)page[kPPW * wave + pp] * kPage + n) * a.n_kv_heads + kvh;
+    const int8_t* krow = a.k_pool + row * kHeadDim + 16 * g;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) kf[pp][c] = *reinterpret_cast<const v4i*>(krow + 64 * c);
+  }
+  const int r16 = tid >> 4, c16 = tid & 15;  // V staging: key r16 of each page, 16-byte chunk c16
+  uint4 vv[kSplitPages];
+#pragma unroll
+  for (int p = 0; p < kSplitPages; ++p) {
+    const long row = ((long)page[p] * kPage + r16) * a.n_kv_heads + kvh;
     vv[p] = *reinterpret_cast<const uint4*>(a.v_pool + row * kHeadDim + 16 * c16);
   }
-  const bool have = j < kPage * nb;
-  {
-    const long row = ((long)page_lds[j >> 4] * kPage + (j & 15)) * a.n_kv_heads + kvh;
-    const int4* src = reinterpret_cast<const int4*>(a.k_pool + row * kHeadDim + 128 * half);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) kr[i] = src[i];
-  }
+  float ksv = 0.f, vsv = 0.f;
   if (tid < kSplitKeys) {
-    const long row = ((long)page_lds[tid >> 4] * kPage + (tid & 15)) * a.n_kv_heads + kvh;
+    const long row = ((long)page[tid >> 4] * kPage + (tid & 15)) * a.n_kv_heads + kvh;
     ksv = a.k_scale[row];
     vsv = a.v_scale[row];
   }
-  const float rowf = tid < G ? a.q_scale[(long)b * a.n_q_heads + kvh * G + tid] * a.row_mul : 0.f;
-  if (r16 < G) *reinterpret_cast<uint4*>(&q_lds[r16][16 * c16]) = qv;
 #pragma unroll
   for (int p = 0; p < kSplitPages; ++p) {
-    const int key = kPage * p + r16;
-    *reinterpret_cast<uint4*>(&v_lds[key][16 * (c16 ^ dswz(key))]) = vv[p];
+    const int key = kPage * (p & 3) + r16;  // key of its 64-key tile
+    *reinterpret_cast<uint4*>(&v_lds[p >> 2][key * kHeadDim + 16 * (c16 ^ swz(key))]) = vv[p];
   }
   if (tid < kSplitKeys) {
     ks_lds[tid] = ksv;
     vs_lds[tid] = vsv;
     lv_lds[tid] = __builtin_amdgcn_logf(vsv);
   }
-  if (tid < G) rowf_lds[tid] = rowf;
-  __syncthreads();
 
-  // ---- scores: thread (key j, half of the channels), int8 dot products
-  {
-    const int p = j >> 4;
-    const bool valid = have && pos_lds[min(p, kSplitPages - 1)] + (j & 15) <= t && first + p < tb.n_total;
-    for (int h = 0; h < G; ++h) {
-      int acc = 0;
-      if (have) {
-        const int4* qq = reinterpret_cast<const int4*>(&q_lds[h][128 * half]);
+  // ---- S^T = K . Q^T for this wave's pages: s[pp] register i is key 4g + i
+  // of page kPPW*wave + pp for head n
+  v4i s[kPPW];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int4 q4 = qq[i];
-          acc = __builtin_amdgcn_sdot4(kr[i].x, q4.x, acc, false);
-          acc = __builtin_amdgcn_sdot4(kr[i].y, q4.y, acc, false);
-          acc = __builtin_amdgcn_sdot4(kr[i].z, q4.z, acc, false);
-          acc = __builtin_amdgcn_sdot4(kr[i].w, q4.w, acc, false);
-        }
-      }
-      acc += __shfl_xor(acc, 1);
-      if (half == 0) s_lds[h][j] = valid ? (float)acc * ks_lds[j] : -INFINITY;
-    }
+  for (int pp = 0; pp < kPPW; ++pp) {
+    s[pp] = v4i{0, 0, 0, 0};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) s[pp] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kf[pp][c], qf[c], s[pp], 0, 0, 0);
   }
   __syncthreads();
 
-  // ---- per head: split max Z of z = s*rowf + log2(v_scale), e = exp2(s*rowf - Z),
-  // l = sum e, P' = e * v_scale, per-page codes.  Wave w takes heads w, w+4, ...
-  for (int h = wave; h < G; h += 4) {
-    const float rowf = rowf_lds[h];
-    float z = -INFINITY;
-    for (int j = lane; j < kSplitKeys; j += 64) {
-      const float s = s_lds[h][j];
-      if (s != -INFINITY) z = fmaxf(z, fmaf(s, rowf, lv_lds[j]));
-    }
+  // ---- scores z = s*k_scale*rowf + log2(v_scale); the split maximum Z per head
+  float sk[kPPW][4];
+  bool ok[kPPW][4];
+  float zmax = -INFINITY;
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) z = fmaxf(z, __shfl_xor(z, off));
-    float lsum = 0.f;
-    for (int j0 = 0; j0 < kSplitKeys; j0 += 64) {
-      const int j = j0 + lane;
-      const float s = s_lds[h][j];
-      const bool ok = s != -INFINITY;
-      const float e = ok ? __builtin_amdgcn_exp2f(fmaf(s, rowf, -z)) : 0.f;
-      const float pv = e * (ok ? vs_lds[j] : 0.f);
+  for (int pp = 0; pp < kPPW; ++pp) {
+    const int p = kPPW * wave + pp;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = kPage * p + 4 * g + i;
+      ok[pp][i] = p < nb && pos[p] + 4 * g + i <= t;
+      sk[pp][i] = (float)s[pp][i] * ks_lds[j];
+      if (ok[pp][i]) zmax = fmaxf(zmax, fmaf(sk[pp][i], rowf, lv_lds[j]));
+    }
+  }
+  zmax = rows_max(zmax);
+  if (g == 0) zpart[wave][n] = zmax;
+  __syncthreads();
+  const float Z = fmaxf(fmaxf(zpart[0][n], zpart[1][n]), fmaxf(zpart[2][n], zpart[3][n]));
+
+  // ---- e = exp2(s*k_scale*rowf - Z) = P, l = sum P, P' = P*v_scale, the
+  // per-page codes rint(P' * 127 / max P') and steps max P' / 127
+  float lsum = 0.f;
+#pragma unroll
+  for (int pp = 0; pp < kPPW; ++pp) {
+    const int p = kPPW * wave + pp;
+    float pv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = kPage * p + 4 * g + i;
+      const float e = ok[pp][i] ? __builtin_amdgcn_exp2f(fmaf(sk[pp][i], rowf, -Z)) : 0.f;
       lsum += e;
-      float mx = pv;  // max over the 16 keys of this page (lanes 16k .. 16k+15)
-#pragma unroll
-      for (int off = 8; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 16));
-      // code = rint(P' * 127 / max); a page whose P' are all zero gets codes 0 and step 0
-      const float c = mx > 0.f ? rintf(pv * (127.0f / mx)) : 0.f;
-      code_lds[h][j] = (int8_t)(int)c;
-      if ((lane & 15) == 0) ps_lds[h][j >> 4] = mx * (1.0f / 127.0f);
+      pv[i] = e * vs_lds[j];
     }
+    const float mx = rows_max(fmaxf(fmaxf(pv[0], pv[1]), fmaxf(pv[2], pv[3])));
+    const float inv = mx > 0.f ? 127.0f / mx : 0.f;  // a page with no attended key: codes 0, step 0
+    uint32_t w = 0;
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) lsum += __shfl_xor(lsum, off);
-    if (lane == 0) {
-      z_lds[h] = z;
-      l_lds[h] = lsum;
-    }
+    for (int i = 0; i < 4; ++i) w |= ((uint32_t)(int32_t)rintf(pv[i] * inv) & 0xffu) << (8 * i);
+    code_lds[n][4 * p + g] = w;
+    if (g == 0) ps_lds[n][p] = mx * (1.0f / 127.0f);
   }
+  lsum = rows_sum(lsum);
+  if (g == 0) lpart[wave][n] = lsum;
   __syncthreads();
 
-  // ---- PV: thread task = (head, 4 channels); int32 sum per page, then ps * sum in float
-  for (int task = tid; task < G * 64; task += 256) {
-    const int h = task >> 6, c4 = 4 * (task & 63);
-    float o[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int p = 0; p < nb; ++p) {
-      int acc[4] = {0, 0, 0, 0};
-#pragma unroll 4
-      for (int r = 0; r < kPage; ++r) {
-        const int key = kPage * p + r;
-        const int code = code_lds[h][key];
-        const uint32_t vv =
-            *reinterpret_cast<const uint32_t*>(&v_lds[key][16 * ((c4 >> 4) ^ dswz(key)) + (c4 & 15)]);
+  // ---- PV with a block-diagonal P operand: row r = 4*hl + pg of row tile rt
+  // is head 4*rt + hl, page pg of the 64-key tile; output register i of lane
+  // (g, n) is then head 4*rt + g, page i, channel 16*nt + n.
+  const int rt_n = (G + 3) >> 2;
+  float o[4][4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] += code * (int)(int8_t)(vv >> (8 * i));
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) o[rt][q] = 0.f;
+#pragma unroll
+  for (int kt = 0; kt < kSplitKeys / kTileKeys; ++kt) {
+    const VFrag read_v(v_lds[kt], lane);
+    v4i vf[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) vf[q] = read_v(4 * wave + q);
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      if (rt >= rt_n) break;
+      const int ha = 4 * rt + (n >> 2), pa = n & 3;  // this lane's row of the P operand
+      const uint32_t cw = ha < G ? code_lds[ha][4 * (4 * kt + pa) + g] : 0u;
+      v4i pa_op = v4i{0, 0, 0, 0};
+#pragma unroll
+      for (int p = 0; p < 4; ++p) pa_op[p] = p == pa ? (int)cw : 0;
+      const int hc = min(4 * rt + g, kMaxDecodeG - 1);  // this lane's head of the result
+      float st[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st[i] = ps_lds[hc][4 * kt + i];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const v4i c = __builtin_amdgcn_mfma_i32_16x16x64_i8(pa_op, vf[q], v4i{0, 0, 0, 0}, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[rt][q] = fmaf(st[i], (float)c[i], o[rt][q]);
       }
-      const float ps = ps_lds[h][p];
+    }
+  }
+
+  // ---- O_s, Z_s and l_s to the workspace
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[i] = fmaf(ps, (float)acc[i], o[i]);
-    }
+  for (int rt = 0; rt < 4; ++rt) {
+    const int h = 4 * rt + g;
+    if (rt >= rt_n || h >= G) continue;
     float* w = ws + ((long)h * a.n_splits + sp) * kWsRow;
-    *reinterpret_cast<float4*>(w + c4) = make_float4(o[0], o[1], o[2], o[3]);
-    if (c4 == 0) {
-      w[kHeadDim] = z_lds[h];
-      w[kHeadDim + 1] = l_lds[h];
-    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) w[16 * (4 * wave + q) + n] = o[rt][q];
+  }
+  if (wave == 0 && g == 0 && n < G) {
+    float* w = ws + ((long)n * a.n_splits + sp) * kWsRow;
+    w[kHeadDim] = Z;
+    w[kHeadDim + 1] = lpart[0][n] + lpart[1][n] + lpart[2][n] + lpart[3][n];
   }
 }
 
 // Combine the splits of one (sequence, query head): weights 2^(Z_s - max Z).
-// One wave per row: the split maxima and weights are found lane-parallel (64
-// splits at a time), then each lane sums 4 channels over the splits.  A
-// sequence with no key to attend (length 0) gets a zero row.
+// Thread c of the 256 sums channel c over the splits; the split weights are
+// formed 256 splits at a time and shared through LDS.  Every split row holds
+// a finite O (an empty split writes zeros and Z = -inf, weight 0), so the sum
+// needs no branch and its loads can all be in flight.  A sequence with no key
+// to attend (length 0) gets a zero row.
 template <bool OUT_BF16>
-__global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
-  __shared__ float f_lds[64];
+__global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
+  __shared__ float f_lds[256];
+  __shared__ float red[4];
   const long row = blockIdx.x;  // sequence * n_q_heads + head
-  const int lane = threadIdx.x, c4 = 4 * lane;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float* w = a.ws + row * a.n_splits * kWsRow;
   float zmax = -INFINITY;
-  for (int s = lane; s < a.n_splits; s += 64) zmax = fmaxf(zmax, w[(long)s * kWsRow + kHeadDim]);
+  for (int s = tid; s < a.n_splits; s += 256) zmax = fmaxf(zmax, w[(long)s * kWsRow + kHeadDim]);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) zmax = fmaxf(zmax, __shfl_xor(zmax, off));
-  float o[4] = {0.f, 0.f, 0.f, 0.f}, l = 0.f;
+  if (lane == 0) red[wave] = zmax;
+  __syncthreads();
+  zmax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  float o = 0.f, l = 0.f;
   if (zmax != -INFINITY) {
-    for (int s0 = 0; s0 < a.n_splits; s0 += 64) {
-      const int s = s0 + lane;
+    for (int s0 = 0; s0 < a.n_splits; s0 += 256) {
+      const int s = s0 + tid;
       float f = 0.f;
       if (s < a.n_splits) {
         const float z = w[(long)s * kWsRow + kHeadDim];
-        if (z != -INFINITY) {  // an empty split wrote only Z and l; its O is not read
-          f = __builtin_amdgcn_exp2f(z - zmax);
-          l = fmaf(f, w[(long)s * kWsRow + kHeadDim + 1], l);
-        }
+        f = __builtin_amdgcn_exp2f(z - zmax);  // 0 for an empty split
+        l = fmaf(f, w[(long)s * kWsRow + kHeadDim + 1], l);
       }
+      __syncthreads();  // the previous chunk's weights are no longer read
+      f_lds[tid] = f;
       __syncthreads();
-      f_lds[lane] = f;
-      __syncthreads();
-      const int n = min(64, a.n_splits - s0);
-#pragma unroll 4
-      for (int i = 0; i < n; ++i) {
-        const float fi = f_lds[i];
-        if (fi == 0.f) continue;  // the same for every lane
-        const float4 v = *reinterpret_cast<const float4*>(w + (long)(s0 + i) * kWsRow + c4);
-        o[0] = fmaf(fi, v.x, o[0]);
-        o[1] = fmaf(fi, v.y, o[1]);
-        o[2] = fmaf(fi, v.z, o[2]);
-        o[3] = fmaf(fi, v.w, o[3]);
-      }
-    }
+      const int m = min(256, a.n_splits - s0);
+      const float* col = w + (long)s0 * kWsRow + tid;
+      int i = 0;
+      for (; i + 8 <= m; i += 8) {
+        float v[8];
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) l += __shfl_xor(l, off);
+        for (int k = 0; k < 8; ++k) v[k] = col[(long)(i + k) * kWsRow];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) o = fmaf(f_lds[i + k], v[k], o);
+      }
+      for (; i < m; ++i) o = fmaf(f_lds[i], col[(long)i * kWsRow], o);
+    }
   }
-  const float inv = l > 0.f ? 1.0f / l : 0.f;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float x = o[i] * inv;
-    if (OUT_BF16) {
-      const uint32_t u32 = __float_as_uint(x);  // round to nearest even
-      reinterpret_cast<uint16_t*>(a.out)[row * kHeadDim + c4 + i] =
-          (uint16_t)((u32 + 0x7fffu + ((u32 >> 16) & 1u)) >> 16);
-    } else {
-      reinterpret_cast<float*>(a.out)[row * kHeadDim + c4 + i] = x;
-    }
+  for (int off = 32; off >= 1; off >>= 1) l += __shfl_xor(l, off);
+  __syncthreads();  // red[] is reused
+  if (lane == 0) red[wave] = l;
+  __syncthreads();
+  l = red[0] + red[1] + red[2] + red[3];
+  const float x = o * (l > 0.f ? 1.0f / l : 0.f);
+  if (OUT_BF16) {
+    const uint32_t u32 = __float_as_uint(x);  // round to nearest even
+    reinterpret_cast<uint16_t*>(a.out)[row * kHeadDim + tid] = (uint16_t)((u32 + 0x7fffu + ((u32 >> 16) & 1u)) >> 16);
+  } else {
+    reinterpret_cast<float*>(a.out)[row * kHeadDim + tid] = x;
   }
 }
 
@@ -281,8 +317,8 @@ hipError_t launch_decode(const DecodeArgs& args_in, bool out_bf16, hipStream_t s
   const unsigned grid = (unsigned)((long)a.batch * a.n_kv_heads * a.n_splits);
   hipLaunchKernelGGL(decode_split_kernel, dim3(grid), dim3(256), 0, stream, a);
   const unsigned rows = (unsigned)((long)a.batch * a.n_q_heads);
-  if (out_bf16) hipLaunchKernelGGL(decode_combine_kernel<true>, dim3(rows), dim3(64), 0, stream, a);
-  else hipLaunchKernelGGL(decode_combine_kernel<false>, dim3(rows), dim3(64), 0, stream, a);
+  if (out_bf16) hipLaunchKernelGGL(decode_combine_kernel<true>, dim3(rows), dim3(256), 0, stream, a);
+  else hipLaunchKernelGGL(decode_combine_kernel<false>, dim3(rows), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
