@@ -4,9 +4,8 @@
 // Q quantization follows the int8 tensor-core prefill attention page, section
 // "Why the attention, and why tensor cores" (one scale per query row).  It is
 // a pure HBM stream: each row is 256 values, read once, written once as int8
-// plus one float scale.  One wave handles two rows, 32 lanes per row, 8
-// values per lane, so every lane issues one 16-byte load (bf16) and one
-// 8-byte store.
+// plus one float scale.  32 lanes take a row, 8 values per lane, so every
+// lane issues one 16-byte load (bf16) and one 8-byte store per row.
 
 #include "wpa_common.h"
 #include "wpa_launch.h"
@@ -46,44 +45,69 @@ __device__ inline uint2 quant8(const float (&v)[8], float& scale) {
   return make_uint2(q_code4(v[0], v[1], v[2], v[3], inv), q_code4(v[4], v[5], v[6], v[7], inv));
 }
 
+// Each half wave takes kRowsPerHalf consecutive rows and issues all their
+// loads before quantizing any, so a wave keeps 4 KB of reads in flight.
+constexpr int kRowsPerHalf = 4;
+
 template <bool BF16>
 __global__ __launch_bounds__(256) void quantize_q_rows_kernel(const void* __restrict__ q,
                                                               int8_t* __restrict__ q_i8,
                                                               float* __restrict__ q_scale,
                                                               long n_rows) {
-  const long row = ((long)blockIdx.x * blockDim.x + threadIdx.x) >> 5;
+  const long row0 = (((long)blockIdx.x * blockDim.x + threadIdx.x) >> 5) * kRowsPerHalf;
   const int sub = threadIdx.x & 31;  // 8 channels each
-  if (row >= n_rows) return;         // whole half-waves drop out together
-  float v[8], scale;
-  load8<BF16>(q, row, sub, v);
-  reinterpret_cast<uint2*>(q_i8)[row * 32 + sub] = quant8(v, scale);
-  if (sub == 0) q_scale[row] = scale;
+  if (row0 >= n_rows) return;        // whole half-waves drop out together
+  float v[kRowsPerHalf][8];
+#pragma unroll
+  for (int i = 0; i < kRowsPerHalf; ++i) load8<BF16>(q, min(row0 + i, n_rows - 1), sub, v[i]);
+#pragma unroll
+  for (int i = 0; i < kRowsPerHalf; ++i) {
+    const long row = row0 + i;
+    float scale;
+    const uint2 codes = quant8(v[i], scale);
+    if (row < n_rows) {
+      reinterpret_cast<uint2*>(q_i8)[row * 32 + sub] = codes;
+      if (sub == 0) q_scale[row] = scale;
+    }
+  }
 }
 
-// KV-pool writer: half wave r takes row r of K (r < n_rows) or row
-// r - n_rows of V, row = token * n_kv_heads + head, and stores its codes and
-// scale at the token's pool slot.  Slots outside the pool are skipped.
+// KV-pool writer: half wave r takes rows kRowsPerHalf*r .. of K, or of V
+// (half waves past the K rows), row = token * n_kv_heads + head, and stores
+// each row's codes and scale at its token's pool slot.  Slots outside the
+// pool are skipped.
 template <bool BF16>
 __global__ __launch_bounds__(256) void kv_write_kernel(const void* __restrict__ k, const void* __restrict__ v,
                                                        const int32_t* __restrict__ slots, int n_kv_heads,
                                                        long n_rows, long n_slots, int8_t* __restrict__ k_pool,
                                                        int8_t* __restrict__ v_pool, float* __restrict__ k_scale,
                                                        float* __restrict__ v_scale) {
-  long r = ((long)blockIdx.x * blockDim.x + threadIdx.x) >> 5;
+  const long halves = (n_rows + kRowsPerHalf - 1) / kRowsPerHalf;  // per tensor
+  long hr = ((long)blockIdx.x * blockDim.x + threadIdx.x) >> 5;
   const int sub = threadIdx.x & 31;
-  if (r >= 2 * n_rows) return;
-  const bool is_v = r >= n_rows;
-  if (is_v) r -= n_rows;
-  const long token = r / n_kv_heads;
-  const int head = (int)(r - token * n_kv_heads);
-  const long slot = slots[token];
-  if (slot < 0 || slot >= n_slots) return;  // the whole half wave skips together
-  float x[8], scale;
-  load8<BF16>(is_v ? v : k, r, sub, x);
-  const uint2 codes = quant8(x, scale);
-  const long dst = slot * n_kv_heads + head;
-  reinterpret_cast<uint2*>(is_v ? v_pool : k_pool)[dst * 32 + sub] = codes;
-  if (sub == 0) (is_v ? v_scale : k_scale)[dst] = scale;
+  if (hr >= 2 * halves) return;
+  const bool is_v = hr >= halves;
+  if (is_v) hr -= halves;
+  const long row0 = hr * kRowsPerHalf;
+  float x[kRowsPerHalf][8];
+  long slot[kRowsPerHalf];
+#pragma unroll
+  for (int i = 0; i < kRowsPerHalf; ++i) {
+    const long r = min(row0 + i, n_rows - 1);
+    slot[i] = slots[r / n_kv_heads];
+    load8<BF16>(is_v ? v : k, r, sub, x[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < kRowsPerHalf; ++i) {
+    const long r = row0 + i;
+    float scale;
+    const uint2 codes = quant8(x[i], scale);
+    if (r >= n_rows || slot[i] < 0 || slot[i] >= n_slots) continue;  // the whole half wave together
+    const long token = r / n_kv_heads;
+    const long dst = slot[i] * n_kv_heads + (r - token * n_kv_heads);
+    reinterpret_cast<uint2*>(is_v ? v_pool : k_pool)[dst * 32 + sub] = codes;
+    if (sub == 0) (is_v ? v_scale : k_scale)[dst] = scale;
+  }
 }
 
 // counts[i] = number of keys row t = q_start + i attends: every listed block
@@ -101,7 +125,7 @@ __global__ __launch_bounds__(256) void mask_counts_kernel(int q_start, int n_tok
 hipError_t launch_quantize_q_rows(const void* q, bool bf16, int n_tokens, int n_q_heads, int8_t* q_i8,
                                   float* q_scale, hipStream_t stream) {
   const long n_rows = (long)n_tokens * n_q_heads;
-  const long threads = n_rows * 32;
+  const long threads = (n_rows + kRowsPerHalf - 1) / kRowsPerHalf * 32;
   const unsigned blocks = (unsigned)((threads + 255) / 256);
   if (bf16)
     hipLaunchKernelGGL(quantize_q_rows_kernel<true>, dim3(blocks), dim3(256), 0, stream, q, q_i8, q_scale, n_rows);
@@ -115,7 +139,7 @@ hipError_t launch_kv_write(const void* k, const void* v, bool bf16, int n_tokens
                            float* v_scale, hipStream_t stream) {
   const long n_rows = (long)n_tokens * n_kv_heads;
   const long n_slots = (long)n_pool_pages * kPage;
-  const long threads = 2 * n_rows * 32;
+  const long threads = 2 * ((n_rows + kRowsPerHalf - 1) / kRowsPerHalf) * 32;
   const unsigned blocks = (unsigned)((threads + 255) / 256);
   if (bf16)
     hipLaunchKernelGGL(kv_write_kernel<true>, dim3(blocks), dim3(256), 0, stream, k, v, slots, n_kv_heads, n_rows,
