@@ -53,6 +53,9 @@ def check_batch(d, out, label, seqs=None):
     ([5, 300, 1500], 4, 1, 0, 0, 52),                     # full causal: up to 94 blocks, 12 splits
     ([40, 1000], 16, 1, 4, 2, 53),                         # 16 query heads per KV head
     ([33, 257], 4, 4, 3, 0, 54),                           # one query head per KV head
+    ([90, 600], 6, 2, 5, 1, 56),                           # 3 heads: a partly filled (head, page) row tile
+    ([129, 520], 16, 2, 6, 0, 57),                         # 8 heads: two row tiles of the PV operand
+    ([64, 400], 10, 2, 0, 0, 58),                          # 5 heads: two row tiles, the second with one head
 ])
 def test_decode_parity(lens, hq, hkv, W, S, seed):
     d = workloads.make_decode_batch(lens, hq, hkv, W, S, seed=seed)
