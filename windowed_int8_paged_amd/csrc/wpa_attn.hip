@@ -517,7 +517,11 @@ __global__ __launch_bounds__(64 * WPG, 4) void row_max_kernel(AttnArgs a, const 
     w.template load_q<HPW, QSrc::kInt8, OUT_BF16>(a, head0, qf, rowf, qscale);
   }
   wait_vmem();
-  WavePages<WPG> pg_next = wave_pages<WPG>(pt, w.tb, w.n_st > 1 ? 1 : 0, w.wave);
+  // page ids three steps ahead: a scalar load still in flight holds up the
+  // step's first LDS wait (both count on lgkmcnt), so it must be issued early
+  // enough to have returned; entries past the list clamp to its last page
+  WavePages<WPG> pg1 = wave_pages<WPG>(pt, w.tb, 1, w.wave), pg2 = wave_pages<WPG>(pt, w.tb, 2, w.wave),
+                 pg3 = wave_pages<WPG>(pt, w.tb, 3, w.wave);
   float* lvs_w = lvs[w.wave];
 
   float zmax[HPW];
@@ -527,8 +531,10 @@ __global__ __launch_bounds__(64 * WPG, 4) void row_max_kernel(AttnArgs a, const 
   for (int it = 0; it + 1 < w.n_st; ++it) {
     wait_stage();
     __syncthreads();
-    issue_stage<WPG, false>(st[buf ^ 1], a, w.plan, w.page_bytes, w.scale_stride, pg_next, w.wave);
-    if (it + 2 < w.n_st) pg_next = wave_pages<WPG>(pt, w.tb, it + 2, w.wave);
+    issue_stage<WPG, false>(st[buf ^ 1], a, w.plan, w.page_bytes, w.scale_stride, pg1, w.wave);
+    pg1 = pg2;
+    pg2 = pg3;
+    pg3 = wave_pages<WPG>(pt, w.tb, it + 4, w.wave);
     rowmax_step<HPW, NP, false>(st[buf], lvs_w, qf, p0, w.lane, w.rc.g, rowf, 0u, zmax);
     buf ^= 1;
   }
@@ -577,7 +583,8 @@ __global__ __launch_bounds__(64 * (WPG / HPW), HPW == 2 ? 1 : 2) void prefill_at
     lsum[h] = 0.f;
   }
   wait_vmem();
-  WavePages<NW> pg_next = wave_pages<NW>(pt, w.tb, w.n_st > 1 ? 1 : 0, w.wave);
+  // page ids two steps ahead (see the row-max launch)
+  WavePages<NW> pg1 = wave_pages<NW>(pt, w.tb, 1, w.wave), pg2 = wave_pages<NW>(pt, w.tb, 2, w.wave);
 
   v4i acc[HPW][2][16];
 #pragma unroll
@@ -590,8 +597,9 @@ __global__ __launch_bounds__(64 * (WPG / HPW), HPW == 2 ? 1 : 2) void prefill_at
   for (int it = 0; it + 1 < w.n_st; ++it) {
     wait_stage();
     __syncthreads();
-    issue_stage<NW, true>(st[buf ^ 1], a, w.plan, w.page_bytes, w.scale_stride, pg_next, w.wave);
-    if (it + 2 < w.n_st) pg_next = wave_pages<NW>(pt, w.tb, it + 2, w.wave);
+    issue_stage<NW, true>(st[buf ^ 1], a, w.plan, w.page_bytes, w.scale_stride, pg1, w.wave);
+    pg1 = pg2;
+    pg2 = wave_pages<NW>(pt, w.tb, it + 3, w.wave);
     pass2_step<HPW, false>(st[buf], qf, w.lane, w.rc.g, rowf, 0u, neg_z, lsum, acc);
     buf ^= 1;
   }
