@@ -14,6 +14,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -31,9 +32,14 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_prefill_attn_32k.json")
 
 
 def kernel_source_hash() -> str:
+    """Hash of the attention kernels' code with comments and blank space removed, so the
+    recorded traffic counters stay attached to a build until its code changes."""
     h = hashlib.sha256()
     for p in ATTN_KERNEL_SOURCES:
-        h.update(open(os.path.join(ROOT, p), "rb").read())
+        text = open(os.path.join(ROOT, p)).read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -34,6 +34,10 @@
 //     whole pages) into row-major XOR-swizzled tiles, double-buffered; LDS
 //     fragment reads are software-pipelined ahead of their matrix products;
 //     V operands are gathered with the transposing read ds_read_b64_tr_b8.
+//   * From bf16 Q (the fused entry point) the row-max launch quantizes each
+//     row once, by the same formula as the separate quantize kernel, and
+//     hands the codes and row scale to the attention launch in the row's
+//     output slot beside Z.
 
 #include "wpa_common.h"
 #include "wpa_lanes.h"
