@@ -468,19 +468,27 @@ struct Work {
 // registers, so four waves share each SIMD.  Every wave takes all WPG query
 // heads of the workgroup and page w*NP .. of each step (a K fragment read
 // once serves WPG products); the WPG partial maxima of a row are combined
-// through LDS at the end.  A step waits for its own copies, syncs (every wave
-// is then done with the other buffer), issues the next step's copies into the
-// other buffer, then computes on its own.
+// through LDS at the end.  A wave copies exactly the pages it reads, so the
+// steps need no barrier: a wave issues the next step's copies into the
+// buffer it read in the previous step, waits with a counted vmcnt until only
+// those are in flight, then computes on this step's buffer.
 //
 // From bf16 Q (QF) wave w quantizes head w only, hands the codes and scale to
 // the attention launch through the row's output slot, and shares them with
 // the other waves through the second stage buffer, which no copy has
 // targeted yet.
+// s_waitcnt immediate for "vmcnt <= n" with expcnt and lgkmcnt left alone
+// (gfx9 layout: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).  Vector
+// loads, the LDS copies among them, complete in issue order, so waiting until
+// at most the newest n are outstanding means every older one has landed.
+constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+
 template <int WPG, bool OUT_BF16, bool QF>
 __global__ __launch_bounds__(64 * WPG, 4) void row_max_kernel(AttnArgs a, const int32_t* __restrict__ pt_arg) {
   constexpr int HPW = WPG;    // query heads per wave
   constexpr int KS = WPG;     // key splits: one per wave
   constexpr int NP = 4 / KS;  // pages of a step per wave
+  constexpr int kCopies = 5 * NP;  // copy instructions a wave issues per step
   __shared__ StageK st[2];
   __shared__ alignas(16) float lvs[WPG][kStepKeys];  // per-wave log2(v_scale) of its pages
   __shared__ float zpart[KS][WPG][16];
@@ -516,6 +524,7 @@ __global__ __launch_bounds__(64 * WPG, 4) void row_max_kernel(AttnArgs a, const 
       for (int c = 0; c < 4; ++c) qf[h][c] = *reinterpret_cast<const v4i*>(src + 64 * c);
       rowf[h] = w.row_ok ? qs_lds[h][w.lane & 15] * a.row_mul : 0.f;
     }
+    __syncthreads();  // every wave has its codes before any copy targets st[1]
   } else {
     float qscale[HPW];
     w.template load_q<HPW, QSrc::kInt8, OUT_BF16>(a, head0, qf, rowf, qscale);
@@ -533,17 +542,19 @@ __global__ __launch_bounds__(64 * WPG, 4) void row_max_kernel(AttnArgs a, const 
   for (int h = 0; h < HPW; ++h) zmax[h] = -INFINITY;
   int buf = 0;
   for (int it = 0; it + 1 < w.n_st; ++it) {
-    wait_stage();
-    __syncthreads();
+    // the other buffer was last read by this wave in the previous step
     issue_stage<WPG, false>(st[buf ^ 1], a, w.plan, w.page_bytes, w.scale_stride, pg1, w.wave);
     pg1 = pg2;
     pg2 = pg3;
     pg3 = wave_pages<WPG>(pt, w.tb, it + 4, w.wave);
+    // this step's copies are done once at most the next step's are in flight
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kCopies));
+    asm volatile("" ::: "memory");
     rowmax_step<HPW, NP, false>(st[buf], lvs_w, qf, p0, w.lane, w.rc.g, rowf, 0u, zmax);
     buf ^= 1;
   }
   wait_stage();
-  __syncthreads();
   rowmax_step<HPW, NP, true>(st[buf], lvs_w, qf, p0, w.lane, w.rc.g, rowf, w.kmask, zmax);
 #pragma unroll
   for (int h = 0; h < HPW; ++h) {
