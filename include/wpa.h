@@ -101,10 +101,7 @@ wpa_status wpa_quantize_q_rows(const void* q, wpa_dtype q_dtype, int n_tokens, i
  *                  Entries must lie in [0, n_pool_pages); this is a caller
  *                  precondition and is not checked on the device.
  *   out            [n_tokens][n_q_heads][256], out_dtype WPA_BF16 (rounded to
- *                  nearest even) or WPA_F32.  The call enqueues two kernels;
- *                  the first leaves a per-row float in the first four bytes of
- *                  each output row, which the second reads and overwrites, so
- *                  out must not alias any input.
+ *                  nearest even) or WPA_F32; must not alias any input.
  * Errors: NULL pointer -> WPA_ERR_NULL; n_tokens < 0, heads <= 0,
  * n_q_heads % n_kv_heads != 0, n_pool_pages < ceil(n_tokens/16),
  * sink_blocks < 0, softmax_scale not finite or <= 0 -> WPA_ERR_SHAPE;
@@ -143,8 +140,8 @@ wpa_status wpa_prefill_attn_i8_chunk(const int8_t* q_i8, const float* q_scale,
                                      void* out, wpa_dtype out_dtype, hipStream_t stream);
 
 /*
- * The attention of wpa_prefill_attn_i8_chunk straight from bf16 Q: the two
- * attention kernels quantize each query row as they load it, with the formula
+ * The attention of wpa_prefill_attn_i8_chunk straight from bf16 Q: the
+ * attention kernel quantizes each query row as it loads it, with the formula
  * of wpa_quantize_q_rows (one scale per row: int8 tensor-core prefill
  * attention page, "Why the attention, and why tensor cores"), so the output
  * is bitwise that of wpa_quantize_q_rows followed by
@@ -152,9 +149,7 @@ wpa_status wpa_prefill_attn_i8_chunk(const int8_t* q_i8, const float* q_scale,
  *   q        [n_tokens][n_q_heads][256] bf16 (q_dtype must be WPA_BF16),
  *            16-byte aligned.  Row i is sequence position q_start + i; pass
  *            q_start = 0 for a whole prompt.
- * The first launch quantizes the rows and leaves their codes and scales in
- * the output rows (with Z) for the second, which overwrites them; out must
- * not alias q.  Other arguments, layouts and errors as
+ * Out must not alias q.  Other arguments, layouts and errors as
  * wpa_prefill_attn_i8_chunk; a q_dtype other than WPA_BF16 ->
  * WPA_ERR_UNSUPPORTED (float32 Q goes through wpa_quantize_q_rows).
  */

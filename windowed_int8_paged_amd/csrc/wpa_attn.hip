@@ -9,35 +9,31 @@
 // <= 0 is full causal attention).
 //
 // gfx950 design
-//   * Two launches over the same per-tile key list.  The first (row max)
-//     computes QK^T and the row maximum Z of score*log2(e) + log2(v_scale)
-//     for every (query row, head) and parks it in the first four bytes of that
-//     row's output; the second (attention) recomputes QK^T, forms P codes and
-//     runs PV.  Knowing Z before any weight is formed makes the row's largest
-//     P*v_scale exactly 1, which fixes the fixed-point scale below.
-//   * One workgroup = one 16-token query tile x one KV head x up to 4 of its
-//     query heads.  In the attention launch a wave takes one head (16 query
-//     rows) and needs at most 256 registers, so two waves share each SIMD; in
-//     the row-max launch a wave takes all four heads and one page of each
-//     step, so each K fragment read from LDS feeds four products, and four
-//     waves share a SIMD.
+//   * One launch.  A workgroup = one 16-token query tile x one KV head x up to
+//     4 of its query heads; a wave takes one head (16 query rows) and needs
+//     at most 256 registers, so two waves share each SIMD.
 //   * Scores are computed transposed, S^T = K . Q^T, with
 //     v_mfma_i32_16x16x64_i8 per 16-key page: a lane holds 4 keys of one query
 //     row per page, so row reductions are in-lane plus lane swaps.
 //   * A step covers 64 keys (four pages).  P codes are exactly the
 //     per-(row, 16-key block) int8 codes of the method; their weights ps*code
-//     are written as one fixed-point integer relative to the row's largest
-//     P*v_scale and split into two signed int8 digit planes, so PV runs at the
+//     are written as one fixed-point integer relative to a per-row reference
+//     2^zref and split into two signed int8 digit planes, so PV runs at the
 //     full K = 64 rate with int32 accumulation across every block and no
 //     per-block floating-point rescale.
+//   * The reference is raised as the scores come in: before a step's weights
+//     are formed, a row whose largest z = score*log2(e) + log2(v_scale) passes
+//     zref gets zref = ceil(z) + 1, and what the row has accumulated (two
+//     int32 planes, l) is shifted right by the whole number of bits zref
+//     moved.  So every P*v_scale stays <= 1 and the row's largest lies within
+//     a factor 4 of it.  P codes depend only on ratios inside their block, so
+//     the reference does not change them.
 //   * K and V pages go global -> LDS by asynchronous LDS DMA (each wave copies
 //     whole pages) into row-major XOR-swizzled tiles, double-buffered; LDS
 //     fragment reads are software-pipelined ahead of their matrix products;
 //     V operands are gathered with the transposing read ds_read_b64_tr_b8.
-//   * From bf16 Q (the fused entry point) the row-max launch quantizes each
-//     row once, by the same formula as the separate quantize kernel, and
-//     hands the codes and row scale to the attention launch in the row's
-//     output slot beside Z.
+//   * From bf16 Q (the fused entry point) each wave quantizes its own rows as
+//     it loads them, by the same formula as the separate quantize kernel.
 
 #include "wpa_common.h"
 #include "wpa_lanes.h"
@@ -58,20 +54,20 @@ constexpr float kCap = 1.0f + 1.0f / 4096.0f;
 constexpr float kFScale = 16777216.0f / kCap;
 constexpr uint32_t kDigitBias = (128u << 16) + (1u << 15);  // digit offset 128, rounding half
 constexpr float kTiny = 0x1p-60f;
-constexpr int kQCodeOffset = 256;  // byte offset of the handed-over Q codes in an output row
+// The per-row reference: raised to ceil(row max) + kRefHeadroom when the
+// row's maximum passes it; shifts of more than kMaxShift bits keep under
+// 2^-22 of the old sums and are capped there (the int32 planes stay exact).
+constexpr float kRefHeadroom = 1.f;
+constexpr float kMaxShift = 22.f;
 
 // Scales of page p of the step: sc[p][0..15] k_scale, sc[p][16..31] v_scale
-// of its 16 keys (one 256-byte copy per page; slots 32..63 repeat them).
+// of its 16 keys (one 256-byte copy per page; slots 32..63 repeat them, and
+// slots 32..47 then take log2(v_scale) of the keys).
 struct alignas(16) Stage {
   int8_t k[kStage];
   int8_t v[kStage];
   float sc[4][64];
 };
-struct alignas(16) StageK {  // the row-max launch stages no V
-  int8_t k[kStage];
-  float sc[4][64];
-};
-
 // Each wave copies 4/WPG whole pages of a step: list entries
 // 4s + wave*PPW + i.  Their physical pages are read through the scalar cache
 // (entries past the end clamp to the last one; their keys are masked).
@@ -221,64 +217,81 @@ __device__ inline void qk_pages_pipelined(const int8_t* kb, const v4i (&qf)[HPW]
   }
 }
 
-// Row-max launch, one step: running max of z = score*log2(e) + log2(v_scale)
-// = (acc*k_scale)*rowf + log2(v_scale) over the wave's NP pages for its HPW
-// heads.  Its row maximum Z makes P' = exp2(z - Z) <= 1 in pass 2, so the
-// row's largest P' is 1 and fixes the fixed-point scale.  Each lane takes one
-// log2 and the wave shares them through its own LDS slice.
-template <int HPW, int NP, bool MASKED, class S>
-__device__ inline void rowmax_step(const S& st, float* lvs_w, const v4i (&qf)[HPW][4], int p0, int lane, int g,
-                                   const float (&rowf)[HPW], uint32_t kmask, float (&zmax)[HPW]) {
-  lvs_w[lane] = __builtin_amdgcn_logf(st.sc[p0 + ((lane >> 4) & (NP - 1))][16 + (lane & 15)]);
-  v4i s[HPW][NP];
-  qk_pages_pipelined<HPW, NP, 4>(st.k, qf, p0, lane, s);
-  __builtin_amdgcn_wave_barrier();
-#pragma unroll
-  for (int pp = 0; pp < NP; ++pp) {
-    const int p = p0 + pp;
-    const float4 ks4 = *reinterpret_cast<const float4*>(&st.sc[p][4 * g]);
-    const float4 lv4 = *reinterpret_cast<const float4*>(&lvs_w[16 * pp + 4 * g]);
-#pragma unroll
-    for (int h = 0; h < HPW; ++h) {
-      float z[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        z[i] = fmaf((float)s[h][pp][i] * (&ks4.x)[i], rowf[h], (&lv4.x)[i]);
-        if (MASKED) z[i] = ((kmask >> (4 * p + i)) & 1u) ? z[i] : -INFINITY;
-      }
-      zmax[h] = fmaxf(fmaxf(zmax[h], fmaxf(z[0], z[1])), fmaxf(z[2], z[3]));
-    }
-  }
-  __builtin_amdgcn_wave_barrier();
-}
-
-// Pass 2, one step for HPW heads: e = exp2(z - Z - log2 v_scale) = P, l += P,
-// P' = P * v_scale <= 1, per-page codes code = rint(P' * 127 / max P'), their
-// weights ps * code as the fixed-point integer x = rint(code * f),
-// f = max P' * Xmax / (127 * cap), split into two signed int8 digit planes
-// x = d0 + 256 d1, then PV.  Every K and V fragment read serves HPW heads.
+// One step for HPW heads.  z = acc*k_scale*rowf + log2(v_scale) (rowf = q
+// scale * softmax scale * log2 e); the row maximum of z over the step raises
+// the reference zref when it passes it (the accumulators and l of a raised
+// row are shifted right by the difference).  Then e = exp2(z - log2 v_scale -
+// zref) = P relative to 2^zref, l += P, P' = P * v_scale <= 1, per-page codes
+// code = rint(P' * 127 / max P'), their weights ps * code as the fixed-point
+// integer x = rint(code * f), f = max P' * Xmax / (127 * cap), split into two
+// signed int8 digit planes x = d0 + 256 d1, then PV.  Every K and V fragment
+// read serves HPW heads.
 //
 // code * f is formed as (code * F + 2^15) >> 16 with F = rint(f * 2^16) < 2^24
 // by one 24-bit multiply-add; with a bias of 128 in the upper half, bytes 2
 // and 3 of the result are d0 + 128 and d1.
 template <int HPW, bool MASKED>
-__device__ inline void pass2_step(const Stage& st, const v4i (&qf)[HPW][4], int lane, int g, const float (&rowf)[HPW],
-                                  uint32_t kmask, const float (&neg_z)[HPW], float (&lsum)[HPW],
-                                  v4i (&acc)[HPW][2][16]) {
+__device__ inline void attn_step(Stage& st, const v4i (&qf)[HPW][4], int lane, int g, const float (&rowf)[HPW],
+                                    uint32_t kmask, float (&zref)[HPW], float (&lsum)[HPW], v4i (&acc)[HPW][2][16]) {
   v4i s[HPW][4];
   qk_pages_pipelined<HPW, 4, 8>(st.k, qf, 0, lane, s);
   v4i dig[HPW][2];
+  // log2(v_scale) of the step's 64 keys, one per lane, into the spare scale
+  // slots (every wave writes the same values)
+  st.sc[lane >> 4][32 + (lane & 15)] = __builtin_amdgcn_logf(st.sc[lane >> 4][16 + (lane & 15)]);
+  __builtin_amdgcn_wave_barrier();
 #pragma unroll
   for (int h = 0; h < HPW; ++h) {
+    float sk[4][4];
+    float zm = -INFINITY;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const float4 ks4 = *reinterpret_cast<const float4*>(&st.sc[p][4 * g]);
+      const float4 lv4 = *reinterpret_cast<const float4*>(&st.sc[p][32 + 4 * g]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sk[p][i] = (float)s[h][p][i] * (&ks4.x)[i];
+        float z = fmaf(sk[p][i], rowf[h], (&lv4.x)[i]);
+        if (MASKED) z = ((kmask >> (4 * p + i)) & 1u) ? z : -INFINITY;
+        zm = fmaxf(zm, z);
+      }
+    }
+    zm = rows_max(zm);
+    // a row whose maximum passes its reference raises it to a whole power of
+    // two plus headroom and scales what it has accumulated by the difference
+    if (__builtin_amdgcn_ballot_w64(zm > zref[h]) != 0) {
+      const bool first = zref[h] == -INFINITY;  // every row starts there: the first step's event
+      const float znew = zm > zref[h] ? ceilf(zm) + kRefHeadroom : zref[h];
+      const int dl = first ? 0 : (int)fminf(znew - zref[h], kMaxShift);
+      lsum[h] = __builtin_amdgcn_ldexpf(lsum[h], -dl);
+      zref[h] = znew;
+      if (!first) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int di = __shfl(dl, 4 * g + i);  // shift of accumulator row 4g + i
+          if (__builtin_amdgcn_ballot_w64(di != 0) != 0) {
+#pragma unroll
+            for (int nt = 0; nt < 16; ++nt) {
+              // lo + 256 hi >> d, exactly: hi keeps its high part, the rest moves to lo
+              const int hi = acc[h][1][nt][i], lo = acc[h][0][nt][i];
+              const int hs = hi >> di;
+              const int rem = hi - (int)((uint32_t)hs << di);
+              acc[h][1][nt][i] = hs;
+              acc[h][0][nt][i] = (lo + (rem << 8)) >> di;
+            }
+          }
+        }
+      }
+    }
+    const float negz = -zref[h];
     float pp[4][4];
     uint32_t mx[4];  // bit patterns of the page maxima of P' >= 0
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-      const float4 ks4 = *reinterpret_cast<const float4*>(&st.sc[p][4 * g]);
       const float4 vs4 = *reinterpret_cast<const float4*>(&st.sc[p][16 + 4 * g]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float e = __builtin_amdgcn_exp2f(fmaf((float)s[h][p][i] * (&ks4.x)[i], rowf[h], neg_z[h]));
+        float e = __builtin_amdgcn_exp2f(fmaf(sk[p][i], rowf[h], negz));
         float pv = e * (&vs4.x)[i];
         if (MASKED) {
           const bool ok = (kmask >> (4 * p + i)) & 1u;
@@ -334,11 +347,9 @@ __device__ inline void pass2_step(const Stage& st, const v4i (&qf)[HPW][4], int 
   }
 }
 
-// Where a launch finds its Q rows: int8 codes and row scales from the
-// caller; bf16 from the caller, quantized on load; or (attention launch of
-// the fused path) the codes and scale the row-max launch left in the row's
-// output slot.
-enum class QSrc { kInt8, kBf16, kOutRow };
+// Where the attention finds its Q rows: int8 codes and row scales from the
+// caller, or bf16 from the caller, quantized on load.
+enum class QSrc { kInt8, kBf16 };
 
 // What a wave knows about its work item: workgroup u covers query tile qt
 // (absolute: the call's rows start at tile a.tile0 of the sequence), KV head
@@ -381,7 +392,7 @@ struct Work {
   // past the end read the last token and are never stored.  From bf16 the
   // lane reads the same 64 channels and the four lanes of a row (lane, +16,
   // +32, +48) share their maximum to quantize the row.
-  template <int H, QSrc QS, bool OUT_BF16>
+  template <int H, QSrc QS>
   __device__ void load_q(const AttnArgs& a, int hd0, v4i (&qf)[H][4], float (&rowf)[H], float (&qscale)[H]) const {
     const int tq = row_ok ? my_t : a.n_tokens - 1;
 #pragma unroll
@@ -431,15 +442,8 @@ struct Work {
         }
         qscale[h] = q_scale_of(amax);
         rowf[h] = row_ok ? qscale[h] * a.row_mul : 0.f;
-        // one head's bf16 row in registers at a time (the row-max launch
-        // runs four waves per SIMD)
+        // one head's bf16 row in registers at a time
         asm volatile("" ::: "memory");
-      } else if (QS == QSrc::kOutRow) {
-        const int8_t* slot = out_row_t<OUT_BF16>(a, tq, hd0 + h);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) qf[h][c] = *reinterpret_cast<const v4i*>(slot + kQCodeOffset + 64 * c + 16 * rc.g);
-        qscale[h] = reinterpret_cast<const float*>(slot)[1];
-        rowf[h] = row_ok ? qscale[h] * a.row_mul : 0.f;
       } else {
         const int8_t* qrow = a.q_i8 + row * kHeadDim + 16 * rc.g;
 #pragma unroll
@@ -449,135 +453,14 @@ struct Work {
       }
     }
   }
-  // The output row of (token t, head hd) as bytes.  Between the launches it
-  // carries the row-max launch's results: Z in bytes 0-3 and, on the fused
-  // path, the Q row scale in bytes 4-7 and the 256 Q codes from byte 256.
-  // The attention launch reads them and then overwrites the row.
-  template <bool OUT_BF16>
-  __device__ int8_t* out_row_t(const AttnArgs& a, int t, int hd) const {
-    const long e = ((long)t * a.n_q_heads + hd) * kHeadDim;
-    return reinterpret_cast<int8_t*>(a.out) + e * (OUT_BF16 ? 2 : 4);
-  }
-  __device__ float* z_slot(const AttnArgs& a, int t, int hd, bool bf16) const {
-    return reinterpret_cast<float*>(bf16 ? out_row_t<true>(a, t, hd) : out_row_t<false>(a, t, hd));
-  }
 };
 
-// First launch, pass 1: the row maximum Z of z over the tile's key list for
-// every (query row, head).  It stages only K and the scales and needs few
-// registers, so four waves share each SIMD.  Every wave takes all WPG query
-// heads of the workgroup and page w*NP .. of each step (a K fragment read
-// once serves WPG products); the WPG partial maxima of a row are combined
-// through LDS at the end.  A wave copies exactly the pages it reads, so the
-// steps need no barrier: a wave issues the next step's copies into the
-// buffer it read in the previous step, waits with a counted vmcnt until only
-// those are in flight, then computes on this step's buffer.
-//
-// From bf16 Q (QF) wave w quantizes head w only, hands the codes and scale to
-// the attention launch through the row's output slot, and shares them with
-// the other waves through the second stage buffer, which no copy has
-// targeted yet.
-// s_waitcnt immediate for "vmcnt <= n" with expcnt and lgkmcnt left alone
-// (gfx9 layout: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).  Vector
-// loads, the LDS copies among them, complete in issue order, so waiting until
-// at most the newest n are outstanding means every older one has landed.
-constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
-
-template <int WPG, bool OUT_BF16, bool QF>
-__global__ __launch_bounds__(64 * WPG, 4) void row_max_kernel(AttnArgs a, const int32_t* __restrict__ pt_arg) {
-  constexpr int HPW = WPG;    // query heads per wave
-  constexpr int KS = WPG;     // key splits: one per wave
-  constexpr int NP = 4 / KS;  // pages of a step per wave
-  constexpr int kCopies = 5 * NP;  // copy instructions a wave issues per step
-  __shared__ StageK st[2];
-  __shared__ alignas(16) float lvs[WPG][kStepKeys];  // per-wave log2(v_scale) of its pages
-  __shared__ float zpart[KS][WPG][16];
-  __shared__ float qs_lds[WPG][16];
-  const WPA_CONST int32_t* pt = (const WPA_CONST int32_t*)pt_arg;
-  Work<WPG, 1> w(a);  // w.head0 is this wave's own head
-  issue_stage<WPG, false>(st[0], a, w.plan, w.page_bytes, w.scale_stride, wave_pages<WPG>(pt, w.tb, 0, w.wave), w.wave);
-
-  const int kh = w.wave;
-  const int head0 = w.head0 - w.wave;  // the workgroup's first head
-  const int p0 = kh * NP;
-  v4i qf[HPW][4];
-  float rowf[HPW];
-  if (QF) {
-    v4i own[1][4];
-    float own_rowf[1], own_scale[1];
-    w.template load_q<1, QSrc::kBf16, OUT_BF16>(a, w.head0, own, own_rowf, own_scale);
-    int8_t* share = st[1].k + (w.wave * kPage + (w.lane & 15)) * kHeadDim + 16 * w.rc.g;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) *reinterpret_cast<v4i*>(share + 64 * c) = own[0][c];
-    if (w.rc.g == 0) qs_lds[w.wave][w.lane] = own_scale[0];
-    if (w.row_ok) {  // hand the codes and the row scale to the attention launch
-      int8_t* slot = w.template out_row_t<OUT_BF16>(a, w.my_t, w.head0);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) *reinterpret_cast<v4i*>(slot + kQCodeOffset + 64 * c + 16 * w.rc.g) = own[0][c];
-      if (w.rc.g == 0) reinterpret_cast<float*>(slot)[1] = own_scale[0];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int h = 0; h < HPW; ++h) {
-      const int8_t* src = st[1].k + (h * kPage + (w.lane & 15)) * kHeadDim + 16 * w.rc.g;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) qf[h][c] = *reinterpret_cast<const v4i*>(src + 64 * c);
-      rowf[h] = w.row_ok ? qs_lds[h][w.lane & 15] * a.row_mul : 0.f;
-    }
-    __syncthreads();  // every wave has its codes before any copy targets st[1]
-  } else {
-    float qscale[HPW];
-    w.template load_q<HPW, QSrc::kInt8, OUT_BF16>(a, head0, qf, rowf, qscale);
-  }
-  wait_vmem();
-  // page ids three steps ahead: a scalar load still in flight holds up the
-  // step's first LDS wait (both count on lgkmcnt), so it must be issued early
-  // enough to have returned; entries past the list clamp to its last page
-  WavePages<WPG> pg1 = wave_pages<WPG>(pt, w.tb, 1, w.wave), pg2 = wave_pages<WPG>(pt, w.tb, 2, w.wave),
-                 pg3 = wave_pages<WPG>(pt, w.tb, 3, w.wave);
-  float* lvs_w = lvs[w.wave];
-
-  float zmax[HPW];
-#pragma unroll
-  for (int h = 0; h < HPW; ++h) zmax[h] = -INFINITY;
-  int buf = 0;
-  for (int it = 0; it + 1 < w.n_st; ++it) {
-    // the other buffer was last read by this wave in the previous step
-    issue_stage<WPG, false>(st[buf ^ 1], a, w.plan, w.page_bytes, w.scale_stride, pg1, w.wave);
-    pg1 = pg2;
-    pg2 = pg3;
-    pg3 = wave_pages<WPG>(pt, w.tb, it + 4, w.wave);
-    // this step's copies are done once at most the next step's are in flight
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kCopies));
-    asm volatile("" ::: "memory");
-    rowmax_step<HPW, NP, false>(st[buf], lvs_w, qf, p0, w.lane, w.rc.g, rowf, 0u, zmax);
-    buf ^= 1;
-  }
-  wait_stage();
-  rowmax_step<HPW, NP, true>(st[buf], lvs_w, qf, p0, w.lane, w.rc.g, rowf, w.kmask, zmax);
-#pragma unroll
-  for (int h = 0; h < HPW; ++h) {
-    const float z = rows_max(zmax[h]);
-    if (w.rc.g == 0) zpart[kh][h][w.lane] = z;
-  }
-  __syncthreads();
-  if (kh == 0 && w.rc.g == 0 && w.row_ok) {
-#pragma unroll
-    for (int h = 0; h < HPW; ++h) {
-      float z = zpart[0][h][w.lane];
-#pragma unroll
-      for (int k = 1; k < KS; ++k) z = fmaxf(z, zpart[k][h][w.lane]);
-      *w.z_slot(a, w.my_t, head0 + h, OUT_BF16) = z;
-    }
-  }
-}
-
-// Second launch: pass 2 over the same key list with K and V staged, P codes,
-// digit planes and PV, then the epilogue.  HPW heads per wave: with HPW = 2 a
-// wave holds two heads' accumulators (256 registers) and runs alone on its
-// SIMD, every K and V fragment it reads feeding two heads; measured slower
-// than HPW = 1 at two waves per SIMD, which is what the launcher uses.
+// The attention: the tile's key list walked four pages at a time with K and V
+// staged, the running reference, P codes, digit planes and PV, then the
+// epilogue.  HPW heads per wave: with HPW = 2 a wave holds two heads'
+// accumulators (256 registers) and runs alone on its SIMD, every K and V
+// fragment it reads feeding two heads; measured slower than HPW = 1 at two
+// waves per SIMD, which is what the launcher uses.
 template <int WPG, int HPW, bool OUT_BF16, bool QF>
 __global__ __launch_bounds__(64 * (WPG / HPW), HPW == 2 ? 1 : 2) void prefill_attn_kernel(
     AttnArgs a, const int32_t* __restrict__ pt_arg) {
@@ -587,18 +470,20 @@ __global__ __launch_bounds__(64 * (WPG / HPW), HPW == 2 ? 1 : 2) void prefill_at
   Work<NW, HPW> w(a);
   issue_stage<NW, true>(st[0], a, w.plan, w.page_bytes, w.scale_stride, wave_pages<NW>(pt, w.tb, 0, w.wave), w.wave);
   v4i qf[HPW][4];
-  float rowf[HPW], neg_z[HPW], lsum[HPW];
+  float rowf[HPW], zref[HPW], lsum[HPW];
   float qscale[HPW];
-  w.template load_q<HPW, QF ? QSrc::kOutRow : QSrc::kInt8, OUT_BF16>(a, w.head0, qf, rowf, qscale);
-  // rows past the end have rowf = 0 and any finite Z; their results stay in
-  // their own accumulator rows and are never stored
+  w.template load_q<HPW, QF ? QSrc::kBf16 : QSrc::kInt8>(a, w.head0, qf, rowf, qscale);
+  // rows past the end read the last token with rowf = 0; their results stay
+  // in their own accumulator rows and are never stored
 #pragma unroll
   for (int h = 0; h < HPW; ++h) {
-    neg_z[h] = w.row_ok ? -*w.z_slot(a, w.my_t, w.head0 + h, OUT_BF16) : 0.f;
+    zref[h] = -INFINITY;  // raised by the first step
     lsum[h] = 0.f;
   }
   wait_vmem();
-  // page ids two steps ahead (see the row-max launch)
+  // page ids two steps ahead: a scalar load still in flight holds up the
+  // step's first LDS wait (both count on lgkmcnt), so it must be issued early
+  // enough to have returned; entries past the list clamp to its last page
   WavePages<NW> pg1 = wave_pages<NW>(pt, w.tb, 1, w.wave), pg2 = wave_pages<NW>(pt, w.tb, 2, w.wave);
 
   v4i acc[HPW][2][16];
@@ -615,12 +500,12 @@ __global__ __launch_bounds__(64 * (WPG / HPW), HPW == 2 ? 1 : 2) void prefill_at
     issue_stage<NW, true>(st[buf ^ 1], a, w.plan, w.page_bytes, w.scale_stride, pg1, w.wave);
     pg1 = pg2;
     pg2 = wave_pages<NW>(pt, w.tb, it + 3, w.wave);
-    pass2_step<HPW, false>(st[buf], qf, w.lane, w.rc.g, rowf, 0u, neg_z, lsum, acc);
+    attn_step<HPW, false>(st[buf], qf, w.lane, w.rc.g, rowf, 0u, zref, lsum, acc);
     buf ^= 1;
   }
   wait_stage();
   __syncthreads();
-  pass2_step<HPW, true>(st[buf], qf, w.lane, w.rc.g, rowf, w.kmask, neg_z, lsum, acc);
+  attn_step<HPW, true>(st[buf], qf, w.lane, w.rc.g, rowf, w.kmask, zref, lsum, acc);
 
   // ---- epilogue: recombine the digit planes, scale by cap / (Xmax * l), store.
   // Output register i of tile nt is row 4g + i, channel 16nt + lane%16.
@@ -652,7 +537,6 @@ __global__ __launch_bounds__(64 * (WPG / HPW), HPW == 2 ? 1 : 2) void prefill_at
 
 template <int WPG, int HPW, bool OUT_BF16, bool QF>
 static void launch_wpg(const AttnArgs& a, unsigned grid, hipStream_t stream) {
-  hipLaunchKernelGGL((row_max_kernel<WPG, OUT_BF16, QF>), dim3(grid), dim3(64 * WPG), 0, stream, a, a.page_table);
   hipLaunchKernelGGL((prefill_attn_kernel<WPG, HPW, OUT_BF16, QF>), dim3(grid), dim3(64 * (WPG / HPW)), 0, stream,
                      a, a.page_table);
 }
@@ -671,8 +555,7 @@ static void launch_wpg(const AttnArgs& a, bool out_bf16, unsigned grid, hipStrea
 hipError_t launch_prefill_attn(const AttnArgs& args_in, bool out_bf16, hipStream_t stream) {
   AttnArgs a = args_in;
   a.G = a.n_q_heads / a.n_kv_heads;
-  // query heads per workgroup: the largest of 4, 2, 1 dividing G; two heads
-  // per wave in pass 2 when that is even
+  // query heads per workgroup: the largest of 4, 2, 1 dividing G, one per wave
   const int wpg = a.G % 4 == 0 ? 4 : (a.G % 2 == 0 ? 2 : 1);
   a.hgroups = a.G / wpg;
   a.n_tiles = (a.n_tokens + kPage - 1) / kPage;
