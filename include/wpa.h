@@ -89,8 +89,10 @@ wpa_status wpa_quantize_q_rows(const void* q, wpa_dtype q_dtype, int n_tokens, i
  *             code_j = rint(P'_j / ps)            (int8, 0..127)
  *     out   = sum_blocks ps * (code . v_i8) / l
  * QK^T and PV run as int8 x int8 -> int32 matrix-core products.  The output
- * matches that formula up to float32 rounding (see the design notes for the
- * error budget); which codes a float32 tie flips is not specified.
+ * matches that formula up to float32 rounding and the rounding of each
+ * block's weights ps * code to a 15-bit fixed point relative to a per-row
+ * power-of-two reference (below 2e-3 of the largest output magnitude on the
+ * tested workloads); which codes a float32 tie flips is not specified.
  *
  *   q_i8, q_scale  from wpa_quantize_q_rows ([n_tokens][n_q_heads][256] int8,
  *                  [n_tokens][n_q_heads] float32); q_i8 16-byte aligned.
