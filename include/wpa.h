@@ -98,7 +98,9 @@ wpa_status wpa_quantize_q_rows(const void* q, wpa_dtype q_dtype, int n_tokens, i
  *                  [n_tokens][n_q_heads] float32); q_i8 16-byte aligned.
  *   k_pool, v_pool [n_pool_pages][16][n_kv_heads][256] int8, 16-byte aligned.
  *   k_scale, v_scale [n_pool_pages][16][n_kv_heads] float32 (per token per KV
- *                  head).  Scales of attended keys must be finite and > 0.
+ *                  head).  Scales of attended keys must be finite and >= 0,
+ *                  v_scale at most 2^64; 0 (what wpa_kv_write_i8 stores for
+ *                  an all-zero row) is allowed.
  *   page_table     [ceil(n_tokens/16)] int32, logical block -> physical page.
  *                  Entries must lie in [0, n_pool_pages); this is a caller
  *                  precondition and is not checked on the device.

@@ -55,10 +55,19 @@ constexpr float kFScale = 16777216.0f / kCap;
 constexpr uint32_t kDigitBias = (128u << 16) + (1u << 15);  // digit offset 128, rounding half
 constexpr float kTiny = 0x1p-60f;
 // The per-row reference: raised to ceil(row max) + kRefHeadroom when the
-// row's maximum passes it; shifts of more than kMaxShift bits keep under
-// 2^-22 of the old sums and are capped there (the int32 planes stay exact).
+// row's maximum passes it.  The two int32 planes of a row hold the value
+// 256 hi + lo; it is divided by 2^d with floor, exactly, in stages of at most
+// kStageShift bits (the carried remainder << 8 stays in int32).  With
+// |256 hi + lo| < 2^40, two stages (kMaxShift bits) take any value to 0 or -1,
+// which is what any larger floor shift gives.
 constexpr float kRefHeadroom = 1.f;
-constexpr float kMaxShift = 22.f;
+constexpr int kStageShift = 22;
+constexpr float kMaxShift = 2.f * kStageShift;
+// log2(v_scale) enters the reference as log2(max(v_scale, kVsFloor)): a zero
+// v_scale (the KV writer's scale of an all-zero V row) still sets a finite
+// reference, and every e = exp2(score * log2(e) - zref) stays below 2^63
+// (P' = e * v_scale is unchanged).
+constexpr float kVsFloor = 0x1p-64f;
 
 // Scales of page p of the step: sc[p][0..15] k_scale, sc[p][16..31] v_scale
 // of its 16 keys (one 256-byte copy per page; slots 32..63 repeat them, and
@@ -230,6 +239,19 @@ __device__ inline void qk_pages_pipelined(const int8_t* kb, const v4i (&qf)[HPW]
 // code * f is formed as (code * F + 2^15) >> 16 with F = rint(f * 2^16) < 2^24
 // by one 24-bit multiply-add; with a bias of 128 in the upper half, bytes 2
 // and 3 of the result are d0 + 128 and d1.
+// Register i of both planes (one accumulator row per 16 lanes) becomes
+// floor((256 hi + lo) / 2^d), exactly, for 0 <= d <= kStageShift: hi keeps
+// its high part and its low d bits move down into lo.
+__device__ inline void shift_planes(v4i (&acc)[2][16], int i, int d) {
+  const int m = (1 << d) - 1;
+#pragma unroll
+  for (int nt = 0; nt < 16; ++nt) {
+    const int hi = acc[1][nt][i], lo = acc[0][nt][i];
+    acc[1][nt][i] = hi >> d;
+    acc[0][nt][i] = (lo + ((hi & m) << 8)) >> d;
+  }
+}
+
 template <int HPW, bool MASKED>
 __device__ inline void attn_step(Stage& st, const v4i (&qf)[HPW][4], int lane, int g, const float (&rowf)[HPW],
                                     uint32_t kmask, float (&zref)[HPW], float (&lsum)[HPW], v4i (&acc)[HPW][2][16]) {
@@ -238,7 +260,7 @@ __device__ inline void attn_step(Stage& st, const v4i (&qf)[HPW][4], int lane, i
   v4i dig[HPW][2];
   // log2(v_scale) of the step's 64 keys, one per lane, into the spare scale
   // slots (every wave writes the same values)
-  st.sc[lane >> 4][32 + (lane & 15)] = __builtin_amdgcn_logf(st.sc[lane >> 4][16 + (lane & 15)]);
+  st.sc[lane >> 4][32 + (lane & 15)] = __builtin_amdgcn_logf(fmaxf(st.sc[lane >> 4][16 + (lane & 15)], kVsFloor));
   __builtin_amdgcn_wave_barrier();
 #pragma unroll
   for (int h = 0; h < HPW; ++h) {
@@ -262,23 +284,18 @@ __device__ inline void attn_step(Stage& st, const v4i (&qf)[HPW][4], int lane, i
     if (__builtin_amdgcn_ballot_w64(zm > zref[h]) != 0) {
       const bool first = zref[h] == -INFINITY;  // every row starts there: the first step's event
       const float znew = zm > zref[h] ? ceilf(zm) + kRefHeadroom : zref[h];
-      const int dl = first ? 0 : (int)fminf(znew - zref[h], kMaxShift);
-      lsum[h] = __builtin_amdgcn_ldexpf(lsum[h], -dl);
+      const float dz = first ? 0.f : znew - zref[h];  // a whole number of bits
+      lsum[h] = __builtin_amdgcn_ldexpf(lsum[h], -(int)fminf(dz, 255.f));
+      const int dl = (int)fminf(dz, kMaxShift);
       zref[h] = znew;
       if (!first) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int di = __shfl(dl, 4 * g + i);  // shift of accumulator row 4g + i
           if (__builtin_amdgcn_ballot_w64(di != 0) != 0) {
-#pragma unroll
-            for (int nt = 0; nt < 16; ++nt) {
-              // lo + 256 hi >> d, exactly: hi keeps its high part, the rest moves to lo
-              const int hi = acc[h][1][nt][i], lo = acc[h][0][nt][i];
-              const int hs = hi >> di;
-              const int rem = hi - (int)((uint32_t)hs << di);
-              acc[h][1][nt][i] = hs;
-              acc[h][0][nt][i] = (lo + (rem << 8)) >> di;
-            }
+            const int d1 = min(di, kStageShift), d2 = di - d1;
+            shift_planes(acc[h], i, d1);
+            if (__builtin_amdgcn_ballot_w64(d2 != 0) != 0) shift_planes(acc[h], i, d2);
           }
         }
       }

@@ -130,7 +130,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   if (tid < kSplitKeys) {
     ks_lds[tid] = ksv;
     vs_lds[tid] = vsv;
-    lv_lds[tid] = __builtin_amdgcn_logf(vsv);
+    // floored as in the prefill kernel: keys of zero v_scale keep Z finite
+    lv_lds[tid] = __builtin_amdgcn_logf(fmaxf(vsv, 0x1p-64f));
   }
 
   // ---- S^T = K . Q^T for this wave's pages: s[pp] register i is key 4g + i
