@@ -48,13 +48,18 @@ def test_mask_counts_chunk_bit_exact(q_start, n, W, S):
     assert np.array_equal(got, oracle.mask_counts(q_start + n, W, S)[q_start:])
 
 
-@pytest.mark.parametrize("W,S", [(3, 1), (0, 0), (2, 4)])
-def test_chunks_equal_one_call_bitwise(W, S):
-    case = workloads.make_case(n_tokens=300, n_q_heads=8, n_kv_heads=2, window_blocks=W, sink_blocks=S,
+@pytest.mark.parametrize("W,S,hq,hkv", [
+    (3, 1, 8, 2), (0, 0, 8, 2), (2, 4, 8, 2),
+    # fewer than four query heads per KV head: a workgroup takes 2 or 4 query
+    # tiles, and the chunk edges (tiles 6 and 13) fall inside those groups
+    (3, 1, 4, 2), (1, 1, 3, 3), (0, 0, 2, 2), (2, 0, 6, 2),
+])
+def test_chunks_equal_one_call_bitwise(W, S, hq, hkv):
+    case = workloads.make_case(n_tokens=300, n_q_heads=hq, n_kv_heads=hkv, window_blocks=W, sink_blocks=S,
                                seed=21, extra_pool_frac=0.25)
     dev = upload(case)
     import windowed_int8_paged_amd as wpa
-    _say(f"chunks vs one call W={W} S={S}")
+    _say(f"chunks vs one call W={W} S={S} hq={hq} hkv={hkv}")
     for dt in (torch.bfloat16, torch.float32):
         q_i8, q_scale = wpa.quantize_q_rows(dev["q_bf16"])
         one = wpa.prefill_attn_i8(q_i8, q_scale, dev["k_pool"], dev["v_pool"], dev["k_scale"], dev["v_scale"],
@@ -67,6 +72,8 @@ def test_chunks_equal_one_call_bitwise(W, S):
     (500, 320, 8, 2, 4, 2, 31),     # ragged chunk at the end, windowed
     (500, 160, 4, 1, 0, 0, 32),     # full causal, chunk in the middle
     (700, 400, 16, 4, 3, 1, 33),    # GQA-4
+    (600, 208, 2, 2, 1, 1, 34),     # MHA, one-block window: four tiles per workgroup, chunk inside a group
+    (600, 96, 4, 2, 2, 0, 35),      # GQA-2: two tiles per workgroup
 ])
 def test_chunk_parity(n_total, q_start, hq, hkv, W, S, seed):
     case = workloads.make_case(n_tokens=n_total, n_q_heads=hq, n_kv_heads=hkv, window_blocks=W, sink_blocks=S,

@@ -9,9 +9,13 @@
 // <= 0 is full causal attention).
 //
 // gfx950 design
-//   * One launch.  A workgroup = one 16-token query tile x one KV head x up to
-//     4 of its query heads; a wave takes one head (16 query rows) and needs
-//     at most 256 registers, so two waves share each SIMD.
+//   * One launch.  A workgroup = four waves on one KV head: 4 of its query
+//     heads on one 16-token query tile, or, with 2 (1) query heads per
+//     workgroup, 2 heads on 2 consecutive tiles (1 head on 4 tiles) walking
+//     the union of their key lists, so every staged K/V page feeds four
+//     waves whatever the GQA ratio.  A wave takes one head of one tile (16
+//     query rows) and needs at most 256 registers, so two waves share each
+//     SIMD.
 //   * Scores are computed transposed, S^T = K . Q^T, with
 //     v_mfma_i32_16x16x64_i8 per 16-key page: a lane holds 4 keys of one query
 //     row per page, so row reductions are in-lane plus lane swaps.
@@ -174,17 +178,21 @@ struct RowCtx {
   int t_mask;  // causal bound of this lane's query row
 };
 
-// Attended keys among the 16 score registers (p, i) of a step; only the last
-// step of a tile holds the diagonal block or empty list slots.
-__device__ inline uint32_t key_mask(const TileBlocks& tb, int step, const RowCtx& rc) {
+// Attended keys among the 16 score registers (p, i) of step `step` of the
+// group's key list tb, for a lane of a wave whose own tile is tw: a block
+// counts if it is one of tw's sinks or lies in tw's window, and a key if it is
+// not after the lane's row.  Only a wave's first and last steps need it.
+__device__ inline uint32_t key_mask(const TileBlocks& tb, const TileBlocks& tw, int step, const RowCtx& rc) {
   uint32_t m = 0;
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     const int li = 4 * step + p;
-    const int blk = li < tb.n_total ? tb.block(li) : 0;
+    const bool listed = li < tb.n_total;
+    const int blk = listed ? tb.block(li) : 0;
+    const bool bok = listed && (blk >= tw.win_start || blk < tw.n_sink);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const bool ok = (li < tb.n_total) && (kPage * blk + 4 * rc.g + i <= rc.t_mask);
+      const bool ok = bok && (kPage * blk + 4 * rc.g + i <= rc.t_mask);
       m |= (ok ? 1u : 0u) << (4 * p + i);
     }
   }
@@ -226,19 +234,6 @@ __device__ inline void qk_pages_pipelined(const int8_t* kb, const v4i (&qf)[HPW]
   }
 }
 
-// One step for HPW heads.  z = acc*k_scale*rowf + log2(v_scale) (rowf = q
-// scale * softmax scale * log2 e); the row maximum of z over the step raises
-// the reference zref when it passes it (the accumulators and l of a raised
-// row are shifted right by the difference).  Then e = exp2(z - log2 v_scale -
-// zref) = P relative to 2^zref, l += P, P' = P * v_scale <= 1, per-page codes
-// code = rint(P' * 127 / max P'), their weights ps * code as the fixed-point
-// integer x = rint(code * f), f = max P' * Xmax / (127 * cap), split into two
-// signed int8 digit planes x = d0 + 256 d1, then PV.  Every K and V fragment
-// read serves HPW heads.
-//
-// code * f is formed as (code * F + 2^15) >> 16 with F = rint(f * 2^16) < 2^24
-// by one 24-bit multiply-add; with a bias of 128 in the upper half, bytes 2
-// and 3 of the result are d0 + 128 and d1.
 // Register i of both planes (one accumulator row per 16 lanes) becomes
 // floor((256 hi + lo) / 2^d), exactly, for 0 <= d <= kStageShift: hi keeps
 // its high part and its low d bits move down into lo.
@@ -252,6 +247,19 @@ __device__ inline void shift_planes(v4i (&acc)[2][16], int i, int d) {
   }
 }
 
+// One step for HPW heads.  z = acc*k_scale*rowf + log2(v_scale) (rowf = q
+// scale * softmax scale * log2 e); the row maximum of z over the step raises
+// the reference zref when it passes it (the accumulators and l of a raised
+// row are shifted right by the difference).  Then e = exp2(z - log2 v_scale -
+// zref) = P relative to 2^zref, l += P, P' = P * v_scale <= 1, per-page codes
+// code = rint(P' * 127 / max P'), their weights ps * code as the fixed-point
+// integer x = rint(code * f), f = max P' * Xmax / (127 * cap), split into two
+// signed int8 digit planes x = d0 + 256 d1, then PV.  Every K and V fragment
+// read serves HPW heads.
+//
+// code * f is formed as (code * F + 2^15) >> 16 with F = rint(f * 2^16) < 2^24
+// by one 24-bit multiply-add; with a bias of 128 in the upper half, bytes 2
+// and 3 of the result are d0 + 128 and d1.
 template <int HPW, bool MASKED>
 __device__ inline void attn_step(Stage& st, const v4i (&qf)[HPW][4], int lane, int g, const float (&rowf)[HPW],
                                     uint32_t kmask, float (&zref)[HPW], float (&lsum)[HPW], v4i (&acc)[HPW][2][16]) {
@@ -368,21 +376,31 @@ __device__ inline void attn_step(Stage& st, const v4i (&qf)[HPW][4], int lane, i
 // caller, or bf16 from the caller, quantized on load.
 enum class QSrc { kInt8, kBf16 };
 
-// What a wave knows about its work item: workgroup u covers query tile qt
-// (absolute: the call's rows start at tile a.tile0 of the sequence), KV head
-// kvh and NW*HPW of its query heads; wave w takes heads head0 .. head0+HPW-1
-// (16 query rows each).  my_t is the lane's row within the call's Q and out,
-// t_abs its position in the sequence.
-template <int NW, int HPW>
+// What a wave knows about its work item.  A workgroup is four waves over
+// TPG = 4/WPG consecutive query tiles and WPG query heads of one KV head:
+// wave w takes head w % WPG of tile T0 + w / WPG (16 query rows), where the
+// group's first tile T0 is a multiple of TPG in the sequence's numbering.
+// The group walks the union of its tiles' key lists, from T0's sinks and
+// window start to the diagonal block of its last tile in the call, so all
+// four waves share every staged page; a wave masks the blocks its own tile
+// does not attend, which can only happen in its first and last steps.
+// Because T0 does not depend on where a call starts, a tile's keys sit at the
+// same list entries in a chunked call as in a whole-sequence call, and its
+// result is the same bits.  The call's rows start at tile a.tile0 of the
+// sequence; my_t is the lane's row within the call's Q and out.  A wave whose
+// tile is outside the call repeats a tile of the call and stores nothing.
+template <int WPG>
 struct Work {
-  int lane, wave, kvh, qt, qt_local, head0, my_t;
-  bool row_ok;
+  static constexpr int TPG = 4 / WPG;
+  int lane, wave, kvh, qt_local, head0, my_t;
+  bool wave_ok, row_ok;
   RowCtx rc;
-  TileBlocks tb;
-  int n_st;  // steps of 64 keys
-  uint32_t kmask;
+  TileBlocks tb;  // the group's key list
+  TileBlocks tw;  // this wave's tile: its sinks and window start
+  int n_st;       // steps of 64 keys
+  int m_early, m_late;  // steps before m_early and from m_late on need key masks
   uint32_t page_bytes, scale_stride;
-  DmaPlan<NW> plan;
+  DmaPlan<4> plan;
   __device__ Work(const AttnArgs& a) {
     lane = threadIdx.x & 63;
     wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -390,19 +408,29 @@ struct Work {
     const int hg = u % a.hgroups;
     u /= a.hgroups;
     kvh = u % a.n_kv_heads;
-    qt_local = a.n_tiles - 1 - u / a.n_kv_heads;  // longest tiles first
-    qt = a.tile0 + qt_local;
-    head0 = kvh * a.G + (hg * NW + wave) * HPW;
+    // tiles in the sequence's numbering; groups of the call, longest first
+    const int t_end = a.tile0 + a.n_tiles - 1;
+    const int t0 = (t_end / TPG - u / a.n_kv_heads) * TPG;
+    const int ta = max(t0, a.tile0), tz = min(t0 + TPG - 1, t_end);  // the group's tiles in the call
+    const int tt = t0 + wave / WPG;
+    wave_ok = tt >= ta && tt <= tz;
+    const int qt = min(max(tt, ta), tz);
+    qt_local = qt - a.tile0;
+    head0 = kvh * a.G + hg * WPG + wave % WPG;
     my_t = qt_local * kPage + (lane & 15);
-    row_ok = my_t < a.n_tokens;
+    row_ok = wave_ok && my_t < a.n_tokens;
     rc.g = lane >> 4;
-    rc.t_mask = kPage * a.tile0 + (row_ok ? my_t : a.n_tokens - 1);
-    tb = tile_blocks(qt, a.window_blocks, a.sink_blocks);
+    rc.t_mask = kPage * a.tile0 + min(my_t, a.n_tokens - 1);
+    tb = tile_blocks(t0, a.window_blocks, a.sink_blocks);
+    tb.n_total = tb.n_sink + (tz + 1 - tb.win_start);
+    tw = tile_blocks(qt, a.window_blocks, a.sink_blocks);
     n_st = (tb.n_total + 3) >> 2;
-    kmask = key_mask(tb, n_st - 1, rc);
+    // list entries of the window blocks before tw's window, and of tw's diagonal block
+    m_early = tw.win_start > tb.win_start ? (tb.n_sink + tw.win_start - tb.win_start + 3) >> 2 : 0;
+    m_late = (tb.n_sink + qt - tb.win_start) >> 2;
     page_bytes = (uint32_t)(kPage * a.n_kv_heads * kHeadDim);
     scale_stride = (uint32_t)(kPage * a.n_kv_heads);
-    make_plan<NW>(plan, a, kvh, wave, lane);
+    make_plan<4>(plan, a, kvh, wave, lane);
   }
   // Q codes of this lane's row for heads hd0 .. in the B-operand layout (16
   // channels per chunk) and rowf = q_scale * softmax_scale * log2(e); rows
@@ -472,20 +500,18 @@ struct Work {
   }
 };
 
-// The attention: the tile's key list walked four pages at a time with K and V
-// staged, the running reference, P codes, digit planes and PV, then the
-// epilogue.  HPW heads per wave: with HPW = 2 a wave holds two heads'
-// accumulators (256 registers) and runs alone on its SIMD, every K and V
-// fragment it reads feeding two heads; measured slower than HPW = 1 at two
-// waves per SIMD, which is what the launcher uses.
-template <int WPG, int HPW, bool OUT_BF16, bool QF>
-__global__ __launch_bounds__(64 * (WPG / HPW), HPW == 2 ? 1 : 2) void prefill_attn_kernel(
-    AttnArgs a, const int32_t* __restrict__ pt_arg) {
-  constexpr int NW = WPG / HPW;
+// The attention: the group's key list walked four pages at a time with K and
+// V staged, the running reference, P codes, digit planes and PV, then the
+// epilogue.  One head per wave (HPW = 1): a wave holding two heads'
+// accumulators runs alone on its SIMD and measured slower than two waves per
+// SIMD.
+template <int WPG, bool OUT_BF16, bool QF>
+__global__ __launch_bounds__(256, 2) void prefill_attn_kernel(AttnArgs a, const int32_t* __restrict__ pt_arg) {
+  constexpr int HPW = 1;
   __shared__ Stage st[2];
   const WPA_CONST int32_t* pt = (const WPA_CONST int32_t*)pt_arg;
-  Work<NW, HPW> w(a);
-  issue_stage<NW, true>(st[0], a, w.plan, w.page_bytes, w.scale_stride, wave_pages<NW>(pt, w.tb, 0, w.wave), w.wave);
+  Work<WPG> w(a);
+  issue_stage<4, true>(st[0], a, w.plan, w.page_bytes, w.scale_stride, wave_pages<4>(pt, w.tb, 0, w.wave), w.wave);
   v4i qf[HPW][4];
   float rowf[HPW], zref[HPW], lsum[HPW];
   float qscale[HPW];
@@ -501,7 +527,7 @@ __global__ __launch_bounds__(64 * (WPG / HPW), HPW == 2 ? 1 : 2) void prefill_at
   // page ids two steps ahead: a scalar load still in flight holds up the
   // step's first LDS wait (both count on lgkmcnt), so it must be issued early
   // enough to have returned; entries past the list clamp to its last page
-  WavePages<NW> pg1 = wave_pages<NW>(pt, w.tb, 1, w.wave), pg2 = wave_pages<NW>(pt, w.tb, 2, w.wave);
+  WavePages<4> pg1 = wave_pages<4>(pt, w.tb, 1, w.wave), pg2 = wave_pages<4>(pt, w.tb, 2, w.wave);
 
   v4i acc[HPW][2][16];
 #pragma unroll
@@ -511,18 +537,31 @@ __global__ __launch_bounds__(64 * (WPG / HPW), HPW == 2 ? 1 : 2) void prefill_at
 #pragma unroll
       for (int nt = 0; nt < 16; ++nt) acc[h][pl][nt] = v4i{0, 0, 0, 0};
   int buf = 0;
-  for (int it = 0; it + 1 < w.n_st; ++it) {
+  // every wave runs n_st steps with one barrier each; only which steps are
+  // masked differs between the waves
+  auto next_stage = [&](int it) {
     wait_stage();
     __syncthreads();
-    issue_stage<NW, true>(st[buf ^ 1], a, w.plan, w.page_bytes, w.scale_stride, pg1, w.wave);
+    if (it + 1 < w.n_st) issue_stage<4, true>(st[buf ^ 1], a, w.plan, w.page_bytes, w.scale_stride, pg1, w.wave);
     pg1 = pg2;
-    pg2 = wave_pages<NW>(pt, w.tb, it + 3, w.wave);
+    pg2 = wave_pages<4>(pt, w.tb, it + 3, w.wave);
+  };
+  int it = 0;
+  for (; it < min(w.m_early, w.n_st); ++it) {
+    next_stage(it);
+    attn_step<HPW, true>(st[buf], qf, w.lane, w.rc.g, rowf, key_mask(w.tb, w.tw, it, w.rc), zref, lsum, acc);
+    buf ^= 1;
+  }
+  for (; it < w.m_late; ++it) {
+    next_stage(it);
     attn_step<HPW, false>(st[buf], qf, w.lane, w.rc.g, rowf, 0u, zref, lsum, acc);
     buf ^= 1;
   }
-  wait_stage();
-  __syncthreads();
-  attn_step<HPW, true>(st[buf], qf, w.lane, w.rc.g, rowf, w.kmask, zref, lsum, acc);
+  for (; it < w.n_st; ++it) {
+    next_stage(it);
+    attn_step<HPW, true>(st[buf], qf, w.lane, w.rc.g, rowf, key_mask(w.tb, w.tw, it, w.rc), zref, lsum, acc);
+    buf ^= 1;
+  }
 
   // ---- epilogue: recombine the digit planes, scale by cap / (Xmax * l), store.
   // Output register i of tile nt is row 4g + i, channel 16nt + lane%16.
@@ -534,7 +573,7 @@ __global__ __launch_bounds__(64 * (WPG / HPW), HPW == 2 ? 1 : 2) void prefill_at
       const int r = 4 * w.rc.g + i;
       const float rr = __shfl(rscale, r);
       const int t = w.qt_local * kPage + r;
-      if (t >= a.n_tokens) continue;
+      if (!w.wave_ok || t >= a.n_tokens) continue;
       const long base = ((long)t * a.n_q_heads + w.head0 + h) * kHeadDim + (w.lane & 15);
 #pragma unroll
       for (int nt = 0; nt < 16; ++nt) {
@@ -552,36 +591,40 @@ __global__ __launch_bounds__(64 * (WPG / HPW), HPW == 2 ? 1 : 2) void prefill_at
   }
 }
 
-template <int WPG, int HPW, bool OUT_BF16, bool QF>
+template <int WPG, bool OUT_BF16, bool QF>
 static void launch_wpg(const AttnArgs& a, unsigned grid, hipStream_t stream) {
-  hipLaunchKernelGGL((prefill_attn_kernel<WPG, HPW, OUT_BF16, QF>), dim3(grid), dim3(64 * (WPG / HPW)), 0, stream,
-                     a, a.page_table);
+  hipLaunchKernelGGL((prefill_attn_kernel<WPG, OUT_BF16, QF>), dim3(grid), dim3(256), 0, stream, a, a.page_table);
 }
-template <int WPG, int HPW>
+template <int WPG>
 static void launch_wpg(const AttnArgs& a, bool out_bf16, unsigned grid, hipStream_t stream) {
   const bool qf = a.q_bf16 != nullptr;
   if (out_bf16) {
-    if (qf) launch_wpg<WPG, HPW, true, true>(a, grid, stream);
-    else launch_wpg<WPG, HPW, true, false>(a, grid, stream);
+    if (qf) launch_wpg<WPG, true, true>(a, grid, stream);
+    else launch_wpg<WPG, true, false>(a, grid, stream);
   } else {
-    if (qf) launch_wpg<WPG, HPW, false, true>(a, grid, stream);
-    else launch_wpg<WPG, HPW, false, false>(a, grid, stream);
+    if (qf) launch_wpg<WPG, false, true>(a, grid, stream);
+    else launch_wpg<WPG, false, false>(a, grid, stream);
   }
 }
 
 hipError_t launch_prefill_attn(const AttnArgs& args_in, bool out_bf16, hipStream_t stream) {
   AttnArgs a = args_in;
   a.G = a.n_q_heads / a.n_kv_heads;
-  // query heads per workgroup: the largest of 4, 2, 1 dividing G, one per wave
+  // query heads per workgroup: the largest of 4, 2, 1 dividing G; the
+  // workgroup's four waves then cover 4 / wpg consecutive query tiles
   const int wpg = a.G % 4 == 0 ? 4 : (a.G % 2 == 0 ? 2 : 1);
+  const int tpg = 4 / wpg;
   a.hgroups = a.G / wpg;
   a.n_tiles = (a.n_tokens + kPage - 1) / kPage;
   a.tile0 = a.q_start / kPage;
   a.row_mul = a.softmax_scale * kLog2e;
-  const unsigned grid = (unsigned)((long)a.n_tiles * a.n_kv_heads * a.hgroups);
-  if (wpg == 4) launch_wpg<4, 1>(a, out_bf16, grid, stream);
-  else if (wpg == 2) launch_wpg<2, 1>(a, out_bf16, grid, stream);
-  else launch_wpg<1, 1>(a, out_bf16, grid, stream);
+  // groups of tpg tiles counted from the sequence's first tile, so that a
+  // chunk's tiles fall in the same groups as in a whole-sequence call
+  const int n_groups = (a.tile0 + a.n_tiles - 1) / tpg - a.tile0 / tpg + 1;
+  const unsigned grid = (unsigned)((long)n_groups * a.n_kv_heads * a.hgroups);
+  if (wpg == 4) launch_wpg<4>(a, out_bf16, grid, stream);
+  else if (wpg == 2) launch_wpg<2>(a, out_bf16, grid, stream);
+  else launch_wpg<1>(a, out_bf16, grid, stream);
   return hipGetLastError();
 }
 
