@@ -1,7 +1,7 @@
 """GPU parity of the fused-Q attention (wpa_prefill_attn_fused_q) through the C ABI.
 
-The entry point takes bf16 Q and quantizes each query row inside the two
-attention kernels with the per-row formula of the int8 tensor-core prefill
+The entry point takes bf16 Q and quantizes each query row inside the
+attention kernel with the per-row formula of the int8 tensor-core prefill
 attention page ("Why the attention, and why tensor cores": one scale per
 row).  Its output must be bitwise that of the separate quantize launch
 followed by the int8-Q attention, and within the acceptance bars of the
@@ -45,9 +45,9 @@ def fused(case, dev, out_dtype, q_start=0, n=None):
 
 CASES = [
     # n, hq, hkv, W, S, seed
-    (64, 2, 1, 0, 0, 41),       # GQA-2: one head per wave in the row-max launch
+    (64, 2, 1, 0, 0, 41),       # GQA-2: two query tiles per workgroup
     (1000, 8, 2, 8, 1, 42),     # GQA-4, windowed, ragged tail
-    (777, 6, 2, 3, 0, 43),      # GQA-3: padded head
+    (777, 6, 2, 3, 0, 43),      # GQA-3: four query tiles per workgroup
     (515, 16, 2, 4, 2, 44),     # GQA-8
     (33, 4, 4, 300, 1, 45),     # MHA, window wider than the sequence
     (1, 4, 2, 0, 0, 46),        # a single token

@@ -86,7 +86,7 @@ SMALL = [
     (64, 2, 1, 0, 0, 1),        # tiny-like, full causal
     (100, 4, 4, 2, 1, 2),       # MHA, ragged tail
     (1000, 8, 2, 8, 1, 3),      # GQA-4, windowed, ragged
-    (777, 6, 2, 3, 0, 4),       # GQA-3 (odd: a padded head), no sink
+    (777, 6, 2, 3, 0, 4),       # GQA-3 (odd: four query tiles per workgroup), no sink
     (515, 16, 2, 4, 2, 5),      # GQA-8 (4 waves per workgroup)
     (300, 2, 2, 1, 0, 6),       # window of one block
     (90, 4, 1, 1, 5, 7),        # sink larger than the window start
