@@ -102,8 +102,10 @@ wpa_status wpa_quantize_q_rows(const void* q, wpa_dtype q_dtype, int n_tokens, i
  *                  v_scale at most 2^64; 0 (what wpa_kv_write_i8 stores for
  *                  an all-zero row) is allowed.
  *   page_table     [ceil(n_tokens/16)] int32, logical block -> physical page.
- *                  Entries must lie in [0, n_pool_pages); this is a caller
- *                  precondition and is not checked on the device.
+ *                  Entries should lie in [0, n_pool_pages); the device clamps
+ *                  an entry outside into it (a wrong page is read, never
+ *                  memory outside the pool), so only the rows that attend
+ *                  such a block are wrong.
  *   out            [n_tokens][n_q_heads][256], out_dtype WPA_BF16 (rounded to
  *                  nearest even) or WPA_F32; must not alias any input.
  * Errors: NULL pointer -> WPA_ERR_NULL; n_tokens < 0, heads <= 0,

@@ -140,6 +140,25 @@ def test_deterministic_and_stray_page_safe():
     assert torch.isfinite(a.float()).all()
 
 
+def test_out_of_pool_page_ids_are_clamped():
+    """Page-table entries outside the pool (negative, past the end) are clamped
+    into it on the device, below 0 to page 0 and past the end to the last page:
+    the output is the oracle's for the clamped table, and nothing outside the
+    pool is read.  The sink block and two window blocks carry bad entries."""
+    import dataclasses
+    case = workloads.make_case(n_tokens=600, n_q_heads=8, n_kv_heads=2, window_blocks=5, sink_blocks=1, seed=13,
+                               extra_pool_frac=0.3, poison_unused=False)
+    n_pool = case.k_pool.shape[0]
+    bad = case.page_table.copy()
+    bad[0], bad[3], bad[20] = 2**31 - 1, -7, n_pool + 1000
+    dev = upload(case)
+    dev["page_table"] = torch.from_numpy(bad).cuda()
+    _say("out-of-pool page ids")
+    _, _, out = run(case, dev, out_dtype=torch.float32)
+    clamped = dataclasses.replace(case, page_table=np.clip(bad, 0, n_pool - 1).astype(np.int32))
+    check_parity(clamped, out, label="clamped page ids")
+
+
 # ---------------------------------------------------------------- the five workloads, sampled
 
 def sample_tiles(n_tokens, window_blocks):

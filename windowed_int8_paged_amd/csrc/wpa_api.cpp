@@ -103,6 +103,7 @@ wpa_status prefill_attn(const int8_t* q_i8, const float* q_scale, const uint16_t
   a.v_scale = v_scale;
   a.page_table = page_table;
   a.out = out;
+  a.n_pool_pages = n_pool_pages;
   a.n_tokens = n_tokens;
   a.n_q_heads = n_q_heads;
   a.n_kv_heads = n_kv_heads;

@@ -83,7 +83,8 @@ struct alignas(16) Stage {
 };
 // Each wave copies 4/WPG whole pages of a step: list entries
 // 4s + wave*PPW + i.  Their physical pages are read through the scalar cache
-// (entries past the end clamp to the last one; their keys are masked).
+// (entries past the end clamp to the last one; their keys are masked).  The
+// copies clamp the page ids themselves into the pool.
 template <int WPG>
 struct WavePages {
   static constexpr int PPW = 4 / WPG;
@@ -160,7 +161,8 @@ __device__ inline void issue_stage(S& st, const AttnArgs& a, const DmaPlan<WPG>&
 #pragma unroll
   for (int i = 0; i < PPW; ++i) {
     const int p = wave * PPW + i;
-    const uint32_t page = (uint32_t)pg.p[i];
+    // a page id outside the pool is clamped into it: a wrong page, never memory outside
+    const uint32_t page = (uint32_t)min(max(pg.p[i], 0), a.n_pool_pages - 1);
     const uint64_t off = (uint64_t)page * page_bytes;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {

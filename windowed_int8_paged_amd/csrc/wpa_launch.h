@@ -17,6 +17,7 @@ struct AttnArgs {
   const float* v_scale;
   const int32_t* page_table;
   void* out;
+  int n_pool_pages;  // page ids are clamped into [0, n_pool_pages)
   int n_tokens, n_q_heads, n_kv_heads;
   int window_blocks, sink_blocks;
   float softmax_scale;
