@@ -91,7 +91,8 @@ wpa_status prefill_attn(const int8_t* q_i8, const float* q_scale, const uint16_t
     return WPA_ERR_UNSUPPORTED;
   if (max_keys_per_row(seq, window_blocks, sink_blocks) > WPA_MAX_KEYS_PER_ROW) return WPA_ERR_UNSUPPORTED;
   const long n_tiles = ceil_div(n_tokens, WPA_PAGE_TOKENS);
-  if (n_tiles * n_kv_heads * ((n_q_heads / n_kv_heads + 1) / 2) > 0x7fffffffL) return WPA_ERR_UNSUPPORTED;
+  if (wpa::prefill_grid(n_q_heads, n_kv_heads, q_start / WPA_PAGE_TOKENS, n_tiles).workgroups > 0x7fffffffL)
+    return WPA_ERR_UNSUPPORTED;
 
   wpa::AttnArgs a = {};
   a.q_i8 = q_i8;

@@ -612,20 +612,16 @@ static void launch_wpg(const AttnArgs& a, bool out_bf16, unsigned grid, hipStrea
 hipError_t launch_prefill_attn(const AttnArgs& args_in, bool out_bf16, hipStream_t stream) {
   AttnArgs a = args_in;
   a.G = a.n_q_heads / a.n_kv_heads;
-  // query heads per workgroup: the largest of 4, 2, 1 dividing G; the
-  // workgroup's four waves then cover 4 / wpg consecutive query tiles
-  const int wpg = a.G % 4 == 0 ? 4 : (a.G % 2 == 0 ? 2 : 1);
-  const int tpg = 4 / wpg;
-  a.hgroups = a.G / wpg;
   a.n_tiles = (a.n_tokens + kPage - 1) / kPage;
   a.tile0 = a.q_start / kPage;
   a.row_mul = a.softmax_scale * kLog2e;
-  // groups of tpg tiles counted from the sequence's first tile, so that a
+  // groups of tiles counted from the sequence's first tile, so that a
   // chunk's tiles fall in the same groups as in a whole-sequence call
-  const int n_groups = (a.tile0 + a.n_tiles - 1) / tpg - a.tile0 / tpg + 1;
-  const unsigned grid = (unsigned)((long)n_groups * a.n_kv_heads * a.hgroups);
-  if (wpg == 4) launch_wpg<4>(a, out_bf16, grid, stream);
-  else if (wpg == 2) launch_wpg<2>(a, out_bf16, grid, stream);
+  const PrefillGrid pg = prefill_grid(a.n_q_heads, a.n_kv_heads, a.tile0, a.n_tiles);
+  a.hgroups = pg.hgroups;
+  const unsigned grid = (unsigned)pg.workgroups;
+  if (pg.wpg == 4) launch_wpg<4>(a, out_bf16, grid, stream);
+  else if (pg.wpg == 2) launch_wpg<2>(a, out_bf16, grid, stream);
   else launch_wpg<1>(a, out_bf16, grid, stream);
   return hipGetLastError();
 }

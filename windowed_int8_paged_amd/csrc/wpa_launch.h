@@ -61,4 +61,23 @@ hipError_t launch_mask_counts(int q_start, int n_tokens, int window_blocks, int 
 // q_bf16 set: the kernels quantize Q as they load it (q_i8, q_scale unused).
 hipError_t launch_prefill_attn(const AttnArgs& args, bool out_bf16, hipStream_t stream);
 
+// Work decomposition of the prefill attention: a workgroup takes wpg query
+// heads of one KV head (the largest of 4, 2, 1 dividing G) on 4/wpg
+// consecutive query tiles, the groups of tiles counted from the sequence's
+// first tile.  Workgroups of a call whose rows start at tile tile0:
+struct PrefillGrid {
+  int wpg, tpg, hgroups;
+  long n_groups, workgroups;
+};
+inline PrefillGrid prefill_grid(int n_q_heads, int n_kv_heads, int tile0, long n_tiles) {
+  PrefillGrid g;
+  const int G = n_q_heads / n_kv_heads;
+  g.wpg = G % 4 == 0 ? 4 : (G % 2 == 0 ? 2 : 1);
+  g.tpg = 4 / g.wpg;
+  g.hgroups = G / g.wpg;
+  g.n_groups = n_tiles > 0 ? (tile0 + n_tiles - 1) / g.tpg - tile0 / g.tpg + 1 : 0;
+  g.workgroups = g.n_groups * n_kv_heads * g.hgroups;
+  return g;
+}
+
 }  // namespace wpa
