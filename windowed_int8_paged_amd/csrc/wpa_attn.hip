@@ -106,6 +106,9 @@ __device__ inline WavePages<WPG> wave_pages(const WPA_CONST int32_t* pt, const T
 // does not model the in-flight LDS write; the kernel orders it explicitly
 // with wait_stage() and a workgroup barrier before any read of that buffer.
 // The 16-byte form takes a scalar base address and a 32-bit per-lane offset.
+// m0 carries the LDS address and is set right before each copy; the compiler
+// warns about clobbering a reserved register, but on gfx950 nothing it emits
+// in these kernels reads m0 (every m0 in their assembly belongs to a copy).
 __device__ inline uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const WPA_LDS void*)p;
 }
