@@ -241,14 +241,19 @@ __device__ inline void qk_pages_pipelined(const int8_t* kb, const v4i (&qf)[HPW]
 
 // Register i of both planes (one accumulator row per 16 lanes) becomes
 // floor((256 hi + lo) / 2^d), exactly, for 0 <= d <= kStageShift: hi keeps
-// its high part and its low d bits move down into lo.
+// its high part and its low d bits move down into lo.  For d >= 1 the sum
+// lo + 256 (hi mod 2^d) is halved first (256 (hi mod 2^d) is even, so
+// floor(lo / 2) + 128 (hi mod 2^d) is the exact half, floored), which keeps
+// every intermediate below 2^31 for any int32 hi and lo; then it is shifted
+// by the remaining d - 1 bits.
 __device__ inline void shift_planes(v4i (&acc)[2][16], int i, int d) {
   const int m = (1 << d) - 1;
+  const int s1 = min(d, 1);
 #pragma unroll
   for (int nt = 0; nt < 16; ++nt) {
     const int hi = acc[1][nt][i], lo = acc[0][nt][i];
     acc[1][nt][i] = hi >> d;
-    acc[0][nt][i] = (lo + ((hi & m) << 8)) >> d;
+    acc[0][nt][i] = (int)((uint32_t)(lo >> s1) + ((uint32_t)(hi & m) << (8 - s1))) >> (d - s1);
   }
 }
 
