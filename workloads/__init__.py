@@ -158,7 +158,9 @@ def make_case(
 
 # The five seeded workloads.  Sizes, heads, window, distributions and pool
 # shapes follow the pages' shapes (hd256, GQA-4, 16-token pages, window 256
-# blocks, contexts 4k/32k/64k) plus a full-causal outlier stress case.
+# blocks, contexts 4k/32k/64k) plus a full-causal outlier stress case.  Two
+# more take the 32k workload's 16 query heads over 8 and 16 KV heads (two and
+# one query heads per KV head): the same int8 work at other GQA ratios.
 CONFIGS = {
     "tiny": dict(n_tokens=64, n_q_heads=2, n_kv_heads=1, window_blocks=0, sink_blocks=0,
                  seed=1001, out_dtype="f32"),
@@ -171,6 +173,10 @@ CONFIGS = {
     "16k_full": dict(n_tokens=16384, n_q_heads=32, n_kv_heads=8, window_blocks=0, sink_blocks=0,
                      seed=1005, scale_lo=1e-3, scale_hi=5e-2, log_uniform_scales=True,
                      q_outlier_frac=0.01, k_saturated_frac=0.02),
+    "32k_gqa2": dict(n_tokens=32768, n_q_heads=16, n_kv_heads=8, window_blocks=256, sink_blocks=1,
+                     seed=1006),
+    "32k_mha": dict(n_tokens=32768, n_q_heads=16, n_kv_heads=16, window_blocks=256, sink_blocks=1,
+                    seed=1007),
 }
 
 
