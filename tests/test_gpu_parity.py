@@ -169,7 +169,7 @@ def sample_tiles(n_tokens, window_blocks):
     return sorted(t for t in tiles if 0 <= t < nt)
 
 
-@pytest.mark.parametrize("name", ["4k", "32k", "64k", "16k_full"])
+@pytest.mark.parametrize("name", ["4k", "32k", "64k", "16k_full", "32k_gqa2", "32k_mha"])
 def test_config_sampled_parity(name):
     case = workloads.make_config(name)
     dev = upload(case)
