@@ -1,4 +1,4 @@
-"""Seeded random shapes through every prefill entry point (C ABI), each checked
+"""Sixteen seeded random shapes through every prefill entry point (C ABI), each checked
 against the oracle at the acceptance bars.
 
 The shapes are drawn once from a fixed seed: lengths from 1 to 1500 tokens
@@ -19,7 +19,7 @@ from gpu_util import check_parity, upload
 pytestmark = pytest.mark.gpu
 
 
-def _shapes(n_cases=10, seed=20261202):
+def _shapes(n_cases=16, seed=20261202):
     rng = np.random.default_rng(seed)
     out = []
     for _ in range(n_cases):
