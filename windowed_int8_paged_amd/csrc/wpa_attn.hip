@@ -9,16 +9,19 @@
 // <= 0 is full causal attention).
 //
 // gfx950 design
-//   * One launch.  A workgroup = four waves on one KV head: 4 of its query
-//     heads on one 16-token query tile, or, with 2 (1) query heads per
-//     workgroup, 2 heads on 2 consecutive tiles (1 head on 4 tiles) walking
-//     the union of their key lists, so every staged K/V page feeds four
+//   * One launch.  A workgroup = eight waves on one KV head: 4 of its query
+//     heads on two consecutive 16-token query tiles, or, with 2 (1) query
+//     heads per workgroup, 2 heads on 4 tiles (1 head on 8 tiles), walking
+//     the union of their key lists, so every staged K/V page feeds eight
 //     waves whatever the GQA ratio.  A wave takes one head of one tile (16
 //     query rows) and needs at most 256 registers, so two waves share each
-//     SIMD.
+//     SIMD and one workgroup fills a CU.
 //   * Scores are computed transposed, S^T = K . Q^T, with
-//     v_mfma_i32_16x16x64_i8 per 16-key page: a lane holds 4 keys of one query
-//     row per page, so row reductions are in-lane plus lane swaps.
+//     v_mfma_i32_16x16x64_i8.  The 16 keys of each product are taken four
+//     from each page of the step, so that afterwards a lane holds one query
+//     row and all 16 keys of one page: a page's maximum is an in-lane
+//     reduction, and the lane's 16 P codes are exactly the A operand of the
+//     PV product (page g of the step in its K-slice 16g .. 16g+15).
 //   * A step covers 64 keys (four pages).  P codes are exactly the
 //     per-(row, 16-key block) int8 codes of the method; their weights ps*code
 //     are written as one fixed-point integer relative to a per-row reference
@@ -32,10 +35,12 @@
 //     moved.  So every P*v_scale stays <= 1 and the row's largest lies within
 //     a factor 4 of it.  P codes depend only on ratios inside their block, so
 //     the reference does not change them.
-//   * K and V pages go global -> LDS by asynchronous LDS DMA (each wave copies
-//     whole pages) into row-major XOR-swizzled tiles, double-buffered; LDS
-//     fragment reads are software-pipelined ahead of their matrix products;
-//     V operands are gathered with the transposing read ds_read_b64_tr_b8.
+//   * K and V pages go global -> LDS by asynchronous LDS DMA into row-major
+//     XOR-swizzled tiles, in a ring of four stages filled three steps ahead.
+//     Each wave issues five copies per step (one page of K or of V and its
+//     scales), so a page is fetched once for all eight waves.  LDS fragment
+//     reads are software-pipelined ahead of their matrix products; V operands
+//     are gathered with the transposing read ds_read_b64_tr_b8.
 //   * From bf16 Q (the fused entry point) each wave quantizes its own rows as
 //     it loads them, by the same formula as the separate quantize kernel.
 
@@ -47,6 +52,10 @@ namespace wpa {
 
 constexpr int kStepKeys = 64;                 // keys per step (four pages)
 constexpr int kStage = kStepKeys * kHeadDim;  // bytes of one staged K or V tile
+constexpr int kWaves = 8;                     // waves per workgroup
+constexpr int kStages = 4;                    // LDS ring depth
+constexpr int kLead = kStages - 1;            // a step's copies are issued this many steps before it runs
+constexpr int kCopies = 5;                    // copies per wave and step (4 x 1 KB rows + 1 scale row)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kKeysPerGroup = 4;              // keys (rows) of one 1 KB copy group
 constexpr float kTwo23 = 8388608.0f;  // 2^23 + v rounds v to an integer held in the low mantissa bits
@@ -73,38 +82,31 @@ constexpr float kMaxShift = 2.f * kStageShift;
 // (P' = e * v_scale is unchanged).
 constexpr float kVsFloor = 0x1p-64f;
 
-// Scales of page p of the step: sc[p][0..15] k_scale, sc[p][16..31] v_scale
-// of its 16 keys (one 256-byte copy per page; slots 32..63 repeat them, and
-// slots 32..47 then take log2(v_scale) of the keys).
+// One stage of the ring: the step's four pages of K and of V (row 16p + s is
+// key s of page p), and their scales: ks[p][s] and vs[p][s] for slot s < 16
+// (each 256-byte copy repeats the page's 16 scales four times), with
+// vs[p][16 + s] then overwritten by log2(v_scale).
 struct alignas(16) Stage {
   int8_t k[kStage];
   int8_t v[kStage];
-  float sc[4][64];
+  float ks[4][64];
+  float vs[4][64];
 };
-// Each wave copies 4/WPG whole pages of a step: list entries
-// 4s + wave*PPW + i.  Their physical pages are read through the scalar cache
-// (entries past the end clamp to the last one; their keys are masked).  The
-// copies clamp the page ids themselves into the pool.
-template <int WPG>
-struct WavePages {
-  static constexpr int PPW = 4 / WPG;
-  int p[PPW];
-};
-template <int WPG>
-__device__ inline WavePages<WPG> wave_pages(const WPA_CONST int32_t* pt, const TileBlocks& tb, int step, int wave) {
-  WavePages<WPG> pg;
-#pragma unroll
-  for (int i = 0; i < WavePages<WPG>::PPW; ++i) {
-    const int li = min(4 * step + wave * WavePages<WPG>::PPW + i, tb.n_total - 1);
-    pg.p[i] = pt[tb.block(li)];
-  }
-  return pg;
+
+// LDS swizzle of the staged tiles: the 16-byte chunk c of row r sits in slot
+// c ^ swz_pg(r).  The score operand reads (rows 16q + 4t + i, q, i = 0..3, for
+// one t) and the transposing V reads (rows 16q + 8h + 0..7 of two adjacent
+// pages q) then touch every bank once per read.  Bit 3 of r does not enter,
+// so the two halves of a V operand (slots k and 8 + k of a page) share one
+// swizzle and one address computation.
+__device__ inline int swz_pg(int r) {
+  return (r & 3) | ((((r >> 2) ^ (r >> 5)) & 1) << 2) | (((r >> 4) & 1) << 3);
 }
 
 // Asynchronous global->LDS copy of 16 (or 4) bytes per lane: lane l's bytes
 // land at lds_base + 16*l (4*l).  Issued as inline assembly so the compiler
 // does not model the in-flight LDS write; the kernel orders it explicitly
-// with wait_stage() and a workgroup barrier before any read of that buffer.
+// with wait_copies() and a workgroup barrier before any read of that buffer.
 // The 16-byte form takes a scalar base address and a 32-bit per-lane offset.
 // m0 carries the LDS address and is set right before each copy; the compiler
 // warns about clobbering a reserved register, but on gfx950 nothing it emits
@@ -119,125 +121,140 @@ __device__ inline void dma16(uint32_t voff, const int8_t* sbase, uint32_t lds_ba
 __device__ inline void dma4(const void* src, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(lds_base) : "memory", "m0");
 }
-// vmcnt(0) through the builtin, so the compiler's own wait tracking sees it:
-// registers filled by earlier vector loads (Q codes, scales) then count as
-// ready, and no wait on the in-flight copies is inserted before their uses.
-__device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-__device__ inline void wait_stage() {
+// Waits until at most N of the wave's vector memory operations are in
+// flight, through the builtin so the compiler's own wait tracking sees it
+// (registers filled by earlier vector loads then count as ready).  The
+// immediate holds vmcnt in bits 3:0 (N < 16 here), with expcnt and lgkmcnt
+// left at their maxima.
+template <int N>
+__device__ inline void wait_vm() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
   asm volatile("" ::: "memory");
-  wait_vmem();
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
   asm volatile("" ::: "memory");
 }
 
-// A wave's copies per step: for each of its pages, four 1 KB row groups
-// (keys 4j .. 4j+3, one 16-byte chunk per lane) of K (and V), and one 256-byte
-// copy of the page's 16 k_scales and 16 v_scales.  The per-lane parts of the
-// addresses are constants kept in registers, so a copy costs one scalar
-// base per page and no vector arithmetic.
-template <int WPG>
+// The copies of one wave: wave w takes page w % 4 of each step, K for waves
+// 0-3 and V for waves 4-7, as four 1 KB row groups (keys 4j .. 4j+3, one
+// 16-byte chunk per lane) and one 256-byte copy of the page's 16 scales.
+// The per-lane parts of the addresses are constants kept in registers, so a
+// copy costs one scalar base per page and no vector arithmetic.
 struct DmaPlan {
-  static constexpr int PPW = 4 / WPG;
-  uint32_t voff[4 * PPW];  // byte offset inside a page, LDS swizzle applied
-  const float* sptr;       // lane l: k_scale (l/16 even) or v_scale (odd) of key l%16 of page 0
+  uint32_t voff[4];     // byte offset inside a page, swizzle applied
+  uint32_t lds_rows;    // offset of the wave's page rows inside a stage
+  uint32_t lds_sc;      // offset of the wave's page scales inside a stage
+  const int8_t* pool;   // k_pool or v_pool
+  const float* sptr;    // lane l: the scale of slot l % 16 of page 0
+  int page;             // page of the step this wave copies (0..3)
 };
-template <int WPG>
-__device__ inline void make_plan(DmaPlan<WPG>& pl, const AttnArgs& a, int kvh, int wave, int lane) {
-  constexpr int PPW = DmaPlan<WPG>::PPW;
+__device__ inline void make_plan(DmaPlan& pl, const AttnArgs& a, int kvh, int wave, int lane) {
   const int q = lane >> 4, s = lane & 15;
+  const int p = wave & 3;
+  const bool is_v = wave >= 4;
   const int row_bytes = a.n_kv_heads * kHeadDim;
 #pragma unroll
-  for (int i = 0; i < PPW; ++i) {
-    const int p = wave * PPW + i;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int rr = 4 * j + q;  // key inside the page
-      pl.voff[4 * i + j] = (uint32_t)(rr * row_bytes + kvh * kHeadDim + 16 * (s ^ swz(16 * p + rr)));
-    }
+  for (int j = 0; j < 4; ++j) {
+    const int rr = 4 * j + q;  // key inside the page
+    pl.voff[j] = (uint32_t)(rr * row_bytes + kvh * kHeadDim + 16 * (s ^ swz_pg(16 * p + rr)));
   }
-  pl.sptr = ((q & 1) ? a.v_scale : a.k_scale) + s * a.n_kv_heads + kvh;
+  pl.lds_rows = (uint32_t)((is_v ? offsetof(Stage, v) : offsetof(Stage, k)) + 16 * p * kHeadDim);
+  pl.lds_sc = (uint32_t)((is_v ? offsetof(Stage, vs) : offsetof(Stage, ks)) + 64 * sizeof(float) * p);
+  pl.pool = is_v ? a.v_pool : a.k_pool;
+  pl.sptr = (is_v ? a.v_scale : a.k_scale) + s * a.n_kv_heads + kvh;
+  pl.page = p;
 }
-
-template <int WPG, bool WITH_V, class S>
-__device__ inline void issue_stage(S& st, const AttnArgs& a, const DmaPlan<WPG>& pl, uint32_t page_bytes,
-                                   uint32_t scale_stride, const WavePages<WPG>& pg, int wave) {
-  constexpr int PPW = DmaPlan<WPG>::PPW;
+// The wave's copies of one step into the stage at LDS address `stage`; a
+// page id outside the pool is clamped into it: a wrong page, never memory
+// outside the pool.
+__device__ inline void issue_copies(uint32_t stage, const AttnArgs& a, const DmaPlan& pl, uint32_t page_bytes,
+                                    uint32_t scale_stride, int page_id) {
+  const uint32_t page = (uint32_t)min(max(page_id, 0), a.n_pool_pages - 1);
+  const uint64_t off = (uint64_t)page * page_bytes;
 #pragma unroll
-  for (int i = 0; i < PPW; ++i) {
-    const int p = wave * PPW + i;
-    // a page id outside the pool is clamped into it: a wrong page, never memory outside
-    const uint32_t page = (uint32_t)min(max(pg.p[i], 0), a.n_pool_pages - 1);
-    const uint64_t off = (uint64_t)page * page_bytes;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      dma16(pl.voff[4 * i + j], a.k_pool + off, lds_addr(st.k + kKeysPerGroup * kHeadDim * (4 * p + j)));
-      if constexpr (WITH_V)
-        dma16(pl.voff[4 * i + j], a.v_pool + off, lds_addr(st.v + kKeysPerGroup * kHeadDim * (4 * p + j)));
-    }
-    dma4(pl.sptr + (uint64_t)page * scale_stride, lds_addr(&st.sc[p][0]));
-  }
+  for (int j = 0; j < 4; ++j) dma16(pl.voff[j], pl.pool + off, stage + pl.lds_rows + kKeysPerGroup * kHeadDim * j);
+  dma4(pl.sptr + (uint64_t)page * scale_stride, stage + pl.lds_sc);
+}
+// Physical page of list entry 4*step + p, read through the scalar cache;
+// entries past the end clamp to the last one (their keys are masked).
+__device__ inline int step_page(const WPA_CONST int32_t* pt, const TileBlocks& tb, int step, int p) {
+  return pt[tb.block(min(4 * step + p, tb.n_total - 1))];
 }
 
 // Per-lane constants of one wave.
 struct RowCtx {
-  int g;       // 16-lane row of the wave (0..3)
+  int g;       // 16-lane row of the wave (0..3); after the scores, also the page it holds
   int t_mask;  // causal bound of this lane's query row
 };
 
-// Attended keys among the 16 score registers (p, i) of step `step` of the
-// group's key list tb, for a lane of a wave whose own tile is tw: a block
-// counts if it is one of tw's sinks or lies in tw's window, and a key if it is
-// not after the lane's row.  Only a wave's first and last steps need it.
+// Attended keys among the lane's 16 scores of step `step` (page g of the
+// step, slot 4t + i in bit 4t + i) of the group's key list tb, for a wave
+// whose own tile is tw: the block counts if it is one of tw's sinks or lies
+// in tw's window, and a key if it is not after the lane's row.  Only a wave's
+// first and last steps need it.
 __device__ inline uint32_t key_mask(const TileBlocks& tb, const TileBlocks& tw, int step, const RowCtx& rc) {
-  uint32_t m = 0;
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const int li = 4 * step + p;
-    const bool listed = li < tb.n_total;
-    const int blk = listed ? tb.block(li) : 0;
-    const bool bok = listed && (blk >= tw.win_start || blk < tw.n_sink);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bool ok = bok && (kPage * blk + 4 * rc.g + i <= rc.t_mask);
-      m |= (ok ? 1u : 0u) << (4 * p + i);
-    }
-  }
-  return m;
+  const int li = 4 * step + rc.g;
+  if (li >= tb.n_total) return 0u;
+  const int blk = tb.block(li);
+  if (blk < tw.win_start && blk >= tw.n_sink) return 0u;
+  const int lim = rc.t_mask - kPage * blk;  // last attended slot
+  return lim >= 15 ? 0xffffu : (lim < 0 ? 0u : (2u << lim) - 1u);
 }
 
-// S^T = K . Q^T for HPW query heads and NP pages (p0 ..) of a step: each K
-// fragment (16 keys x 64 channels, one ds_read_b128) feeds HPW products.
-// Afterwards s[h][pp] register i of lane l holds query row l%16 and key
-// 4(l/16) + i of page p0 + pp.  The fragment reads are software-pipelined D
-// fragments ahead of their products; the scheduling fences keep the compiler
-// from sinking them back next to their uses (it would otherwise reuse one
-// register set and wait out the full LDS latency before every product).
-template <int HPW, int NP, int D>
-__device__ inline void qk_pages_pipelined(const int8_t* kb, const v4i (&qf)[HPW][4], int p0, int lane,
-                                          v4i (&s)[HPW][NP]) {
-  constexpr int NF = 4 * NP;  // fragments: f = 4 * pp + c
-  const int g = lane >> 4;
-  auto read = [&](int f) {
-    const int r = 16 * (p0 + f / 4) + (lane & 15);
-    const int slot = (4 * (f % 4) + g) ^ swz(r);
+// S^T = K . Q^T for the 64 keys of a step.  Product t takes, as its 16 keys
+// m = 0..15, slot 4t + m%4 of page m/4, so that afterwards register i of
+// s[t] in lane l holds query row l%16 and slot 4t + i of page l/16.  Each K
+// fragment (16 keys x 64 channels) is one ds_read_b128.  The fragment reads
+// are software-pipelined D fragments ahead of their products; the scheduling
+// fences keep the compiler from sinking them back next to their uses (it
+// would otherwise reuse one register set and wait out the full LDS latency
+// before every product).
+template <int D>
+__device__ inline void qk_step(const int8_t* kb, const v4i (&qf)[4], int lane, v4i (&s)[4]) {
+  const int m = lane & 15, kg = lane >> 4;
+  auto read = [&](int f) {  // fragment f = 4t + c: product t, channel chunk c
+    const int t = f >> 2, c = f & 3;
+    const int r = 16 * (m >> 2) + 4 * t + (m & 3);
+    const int slot = (4 * c + kg) ^ swz_pg(r);
     return *reinterpret_cast<const v4i*>(kb + r * kHeadDim + 16 * slot);
   };
-  v4i kf[NF];
+  v4i kf[16];
 #pragma unroll
   for (int f = 0; f < D; ++f) {
     kf[f] = read(f);
     __builtin_amdgcn_sched_barrier(0);  // issue in order: the first product waits for the first read only
   }
 #pragma unroll
-  for (int f = 0; f < NF; ++f) {
-    if (f + D < NF) kf[f + D] = read(f + D);
+  for (int f = 0; f < 16; ++f) {
+    if (f + D < 16) kf[f + D] = read(f + D);
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int h = 0; h < HPW; ++h)
-      s[h][f / 4] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kf[f], qf[h][f % 4], f % 4 ? s[h][f / 4] : v4i{0, 0, 0, 0},
-                                                          0, 0, 0);
+    s[f >> 2] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kf[f], qf[f & 3], (f & 3) ? s[f >> 2] : v4i{0, 0, 0, 0}, 0,
+                                                     0, 0);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
+
+// B operand of a PV product over one staged 64-key V tile: lane (column j,
+// row group g) gets channel 16 nt + j of the 16 keys of page g in slot order,
+// which is the order of the lane's P operand.  Within a 16-lane group, the
+// transposing read gives lane j byte j%8 of the 8-byte blocks addressed by
+// lanes 2k + j/8 (k = 0..7); lane L here addresses slot L/2 of page g (slot
+// 8 + L/2 in the second read) at channel 16 nt + 8 (L%2).
+struct VFragPg {
+  const int8_t* row1;
+  int sw;
+  __device__ VFragPg(const int8_t* tile, int lane) {
+    const int g = lane >> 4, j = lane & 15;
+    const int key1 = 16 * g + (j >> 1);
+    row1 = tile + key1 * kHeadDim + 8 * (j & 1);
+    sw = swz_pg(key1);  // = swz_pg(key1 + 8)
+  }
+  __device__ v4i operator()(int nt) const {
+    const int8_t* p = row1 + 16 * (nt ^ sw);
+    const v2i lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32((WPA_LDS v2i*)p);
+    const v2i hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32((WPA_LDS v2i*)(p + 8 * kHeadDim));  // key1 + 8
+    return v4i{lo.x, lo.y, hi.x, hi.y};
+  }
+};
 
 // Register i of both planes (one accumulator row per 16 lanes) becomes
 // floor((256 hi + lo) / 2^d), exactly, for 0 <= d <= kStageShift: hi keeps
@@ -257,112 +274,107 @@ __device__ inline void shift_planes(v4i (&acc)[2][16], int i, int d) {
   }
 }
 
-// One step for HPW heads.  z = acc*k_scale*rowf + log2(v_scale) (rowf = q
+// One step of one wave.  z = acc*k_scale*rowf + log2(v_scale) (rowf = q
 // scale * softmax scale * log2 e); the row maximum of z over the step raises
 // the reference zref when it passes it (the accumulators and l of a raised
 // row are shifted right by the difference).  Then e = exp2(z - log2 v_scale -
 // zref) = P relative to 2^zref, l += P, P' = P * v_scale <= 1, per-page codes
 // code = rint(P' * 127 / max P'), their weights ps * code as the fixed-point
 // integer x = rint(code * f), f = max P' * Xmax / (127 * cap), split into two
-// signed int8 digit planes x = d0 + 256 d1, then PV.  Every K and V fragment
-// read serves HPW heads.
+// signed int8 digit planes x = d0 + 256 d1, then PV.
 //
 // code * f is formed as (code * F + 2^15) >> 16 with F = rint(f * 2^16) < 2^24
 // by one 24-bit multiply-add; with a bias of 128 in the upper half, bytes 2
 // and 3 of the result are d0 + 128 and d1.
-template <int HPW, bool MASKED>
-__device__ inline void attn_step(Stage& st, const v4i (&qf)[HPW][4], int lane, int g, const float (&rowf)[HPW],
-                                    uint32_t kmask, float (&zref)[HPW], float (&lsum)[HPW], v4i (&acc)[HPW][2][16]) {
-  v4i s[HPW][4];
-  qk_pages_pipelined<HPW, 4, 8>(st.k, qf, 0, lane, s);
-  v4i dig[HPW][2];
+template <bool MASKED>
+__device__ inline void attn_step(Stage& st, const v4i (&qf)[4], int lane, int g, float rowf, uint32_t kmask,
+                                 float& zref, float& lsum, v4i (&acc)[2][16]) {
+  v4i s[4];
+  qk_step<8>(st.k, qf, lane, s);
   // log2(v_scale) of the step's 64 keys, one per lane, into the spare scale
   // slots (every wave writes the same values)
-  st.sc[lane >> 4][32 + (lane & 15)] = __builtin_amdgcn_logf(fmaxf(st.sc[lane >> 4][16 + (lane & 15)], kVsFloor));
+  st.vs[lane >> 4][16 + (lane & 15)] = __builtin_amdgcn_logf(fmaxf(st.vs[lane >> 4][lane & 15], kVsFloor));
   __builtin_amdgcn_wave_barrier();
+  float sk[4][4];
+  float zm = -INFINITY;
 #pragma unroll
-  for (int h = 0; h < HPW; ++h) {
-    float sk[4][4];
-    float zm = -INFINITY;
+  for (int t = 0; t < 4; ++t) {
+    const float4 ks4 = *reinterpret_cast<const float4*>(&st.ks[g][4 * t]);
+    const float4 lv4 = *reinterpret_cast<const float4*>(&st.vs[g][16 + 4 * t]);
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const float4 ks4 = *reinterpret_cast<const float4*>(&st.sc[p][4 * g]);
-      const float4 lv4 = *reinterpret_cast<const float4*>(&st.sc[p][32 + 4 * g]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sk[p][i] = (float)s[h][p][i] * (&ks4.x)[i];
-        float z = fmaf(sk[p][i], rowf[h], (&lv4.x)[i]);
-        if (MASKED) z = ((kmask >> (4 * p + i)) & 1u) ? z : -INFINITY;
-        zm = fmaxf(zm, z);
-      }
-    }
-    zm = rows_max(zm);
-    // a row whose maximum passes its reference raises it to a whole power of
-    // two plus headroom and scales what it has accumulated by the difference
-    if (__builtin_amdgcn_ballot_w64(zm > zref[h]) != 0) {
-      const bool first = zref[h] == -INFINITY;  // every row starts there: the first step's event
-      const float znew = zm > zref[h] ? ceilf(zm) + kRefHeadroom : zref[h];
-      const float dz = first ? 0.f : znew - zref[h];  // a whole number of bits
-      lsum[h] = __builtin_amdgcn_ldexpf(lsum[h], -(int)fminf(dz, 255.f));
-      const int dl = (int)fminf(dz, kMaxShift);
-      zref[h] = znew;
-      if (!first) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int di = __shfl(dl, 4 * g + i);  // shift of accumulator row 4g + i
-          if (__builtin_amdgcn_ballot_w64(di != 0) != 0) {
-            const int d1 = min(di, kStageShift), d2 = di - d1;
-            shift_planes(acc[h], i, d1);
-            if (__builtin_amdgcn_ballot_w64(d2 != 0) != 0) shift_planes(acc[h], i, d2);
-          }
-        }
-      }
-    }
-    const float negz = -zref[h];
-    float pp[4][4];
-    uint32_t mx[4];  // bit patterns of the page maxima of P' >= 0
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const float4 vs4 = *reinterpret_cast<const float4*>(&st.sc[p][16 + 4 * g]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float e = __builtin_amdgcn_exp2f(fmaf(sk[p][i], rowf[h], negz));
-        float pv = e * (&vs4.x)[i];
-        if (MASKED) {
-          const bool ok = (kmask >> (4 * p + i)) & 1u;
-          e = ok ? e : 0.f;
-          pv = ok ? pv : 0.f;
-        }
-        lsum[h] += e;
-        pp[p][i] = pv;
-      }
-      mx[p] = max(max(__float_as_uint(pp[p][0]), __float_as_uint(pp[p][1])),
-                  max(__float_as_uint(pp[p][2]), __float_as_uint(pp[p][3])));
-    }
-    page_maxima(mx);
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      // a page whose P' all lie below 2^-60 (masked ones are 0) gets F = 0 and
-      // finite codes, so its weights are exactly zero
-      const float inv = 127.0f * __builtin_amdgcn_rcpf(__uint_as_float(max(mx[p], __float_as_uint(kTiny))));
-      const uint32_t F = (uint32_t)fmaf(__uint_as_float(mx[p]), kFScale, 0.5f);
-      uint32_t r[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t code = __float_as_uint(fmaf(pp[p][i], inv, kTwo23));  // 2^23 + rint(P' * inv)
-        r[i] = __umul24(code, F) + kDigitBias;
-      }
-      const uint32_t w01 = __builtin_amdgcn_perm(r[1], r[0], 0x07060302u);
-      const uint32_t w23 = __builtin_amdgcn_perm(r[3], r[2], 0x07060302u);
-      dig[h][0][p] = (int)(__builtin_amdgcn_perm(w23, w01, 0x06040200u) ^ 0x80808080u);  // low digit, signed
-      dig[h][1][p] = (int)__builtin_amdgcn_perm(w23, w01, 0x07050301u);                 // high digit
+    for (int i = 0; i < 4; ++i) {
+      sk[t][i] = (float)s[t][i] * (&ks4.x)[i];
+      float z = fmaf(sk[t][i], rowf, (&lv4.x)[i]);
+      if (MASKED) z = ((kmask >> (4 * t + i)) & 1u) ? z : -INFINITY;
+      zm = fmaxf(zm, z);
     }
   }
+  zm = rows_max(zm);
+  // a row whose maximum passes its reference raises it to a whole power of
+  // two plus headroom and scales what it has accumulated by the difference
+  if (__builtin_amdgcn_ballot_w64(zm > zref) != 0) {
+    const bool first = zref == -INFINITY;  // every row starts there: the first step's event
+    const float znew = zm > zref ? ceilf(zm) + kRefHeadroom : zref;
+    const float dz = first ? 0.f : znew - zref;  // a whole number of bits
+    lsum = __builtin_amdgcn_ldexpf(lsum, -(int)fminf(dz, 255.f));
+    const int dl = (int)fminf(dz, kMaxShift);
+    zref = znew;
+    if (!first) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int di = __shfl(dl, 4 * g + i);  // shift of accumulator row 4g + i
+        if (__builtin_amdgcn_ballot_w64(di != 0) != 0) {
+          const int d1 = min(di, kStageShift), d2 = di - d1;
+          shift_planes(acc, i, d1);
+          if (__builtin_amdgcn_ballot_w64(d2 != 0) != 0) shift_planes(acc, i, d2);
+        }
+      }
+    }
+  }
+  const float negz = -zref;
+  float pp[4][4];
+  uint32_t mx = 0;  // bit pattern of the page maximum of P' >= 0
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const float4 vs4 = *reinterpret_cast<const float4*>(&st.vs[g][4 * t]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float e = __builtin_amdgcn_exp2f(fmaf(sk[t][i], rowf, negz));
+      float pv = e * (&vs4.x)[i];
+      if (MASKED) {
+        const bool ok = (kmask >> (4 * t + i)) & 1u;
+        e = ok ? e : 0.f;
+        pv = ok ? pv : 0.f;
+      }
+      lsum += e;
+      pp[t][i] = pv;
+    }
+    mx = max(mx, max(max(__float_as_uint(pp[t][0]), __float_as_uint(pp[t][1])),
+                     max(__float_as_uint(pp[t][2]), __float_as_uint(pp[t][3]))));
+  }
+  // a page whose P' all lie below 2^-60 (masked ones are 0) gets F = 0 and
+  // finite codes, so its weights are exactly zero
+  const float inv = 127.0f * __builtin_amdgcn_rcpf(__uint_as_float(max(mx, __float_as_uint(kTiny))));
+  const uint32_t F = (uint32_t)fmaf(__uint_as_float(mx), kFScale, 0.5f);
+  v4i dig[2];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    uint32_t r[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t code = __float_as_uint(fmaf(pp[t][i], inv, kTwo23));  // 2^23 + rint(P' * inv)
+      r[i] = __umul24(code, F) + kDigitBias;
+    }
+    const uint32_t w01 = __builtin_amdgcn_perm(r[1], r[0], 0x07060302u);
+    const uint32_t w23 = __builtin_amdgcn_perm(r[3], r[2], 0x07060302u);
+    dig[0][t] = (int)(__builtin_amdgcn_perm(w23, w01, 0x06040200u) ^ 0x80808080u);  // low digit, signed
+    dig[1][t] = (int)__builtin_amdgcn_perm(w23, w01, 0x07050301u);                 // high digit
+  }
 
-  // V operand (see VFrag): reads run two column tiles ahead of their products
-  // (see qk_pages_pipelined)
+  // V operand (see VFragPg): reads run two column tiles ahead of their
+  // products (see qk_step)
   constexpr int DV = 2;
-  const VFrag read_v(st.v, lane);
+  const VFragPg read_v(st.v, lane);
   v4i vf[16];
 #pragma unroll
   for (int nt = 0; nt < DV; ++nt) {
@@ -373,11 +385,8 @@ __device__ inline void attn_step(Stage& st, const v4i (&qf)[HPW][4], int lane, i
   for (int nt = 0; nt < 16; ++nt) {
     if (nt + DV < 16) vf[nt + DV] = read_v(nt + DV);
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int h = 0; h < HPW; ++h) {
-      acc[h][0][nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(dig[h][0], vf[nt], acc[h][0][nt], 0, 0, 0);
-      acc[h][1][nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(dig[h][1], vf[nt], acc[h][1][nt], 0, 0, 0);
-    }
+    acc[0][nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(dig[0], vf[nt], acc[0][nt], 0, 0, 0);
+    acc[1][nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(dig[1], vf[nt], acc[1][nt], 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -386,13 +395,13 @@ __device__ inline void attn_step(Stage& st, const v4i (&qf)[HPW][4], int lane, i
 // caller, or bf16 from the caller, quantized on load.
 enum class QSrc { kInt8, kBf16 };
 
-// What a wave knows about its work item.  A workgroup is four waves over
-// TPG = 4/WPG consecutive query tiles and WPG query heads of one KV head:
+// What a wave knows about its work item.  A workgroup is eight waves over
+// TPG = 8/WPG consecutive query tiles and WPG query heads of one KV head:
 // wave w takes head w % WPG of tile T0 + w / WPG (16 query rows), where the
 // group's first tile T0 is a multiple of TPG in the sequence's numbering.
 // The group walks the union of its tiles' key lists, from T0's sinks and
 // window start to the diagonal block of its last tile in the call, so all
-// four waves share every staged page; a wave masks the blocks its own tile
+// eight waves share every staged page; a wave masks the blocks its own tile
 // does not attend, which can only happen in its first and last steps.
 // Because T0 does not depend on where a call starts, a tile's keys sit at the
 // same list entries in a chunked call as in a whole-sequence call, and its
@@ -401,8 +410,9 @@ enum class QSrc { kInt8, kBf16 };
 // tile is outside the call repeats a tile of the call and stores nothing.
 template <int WPG>
 struct Work {
-  static constexpr int TPG = 4 / WPG;
+  static constexpr int TPG = kWaves / WPG;
   int lane, wave, kvh, qt_local, head0, my_t;
+  bool valid;  // false for the few padding workgroups past the last group
   bool wave_ok, row_ok;
   RowCtx rc;
   TileBlocks tb;  // the group's key list
@@ -410,17 +420,18 @@ struct Work {
   int n_st;       // steps of 64 keys
   int m_early, m_late;  // steps before m_early and from m_late on need key masks
   uint32_t page_bytes, scale_stride;
-  DmaPlan<4> plan;
+  DmaPlan plan;
   __device__ Work(const AttnArgs& a) {
     lane = threadIdx.x & 63;
     wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    int u = blockIdx.x;
-    const int hg = u % a.hgroups;
-    u /= a.hgroups;
-    kvh = u % a.n_kv_heads;
+    long stream, group;
+    prefill_item(blockIdx.x, a.streams, a.xcd_r, a.xcd_q, stream, group);
+    valid = group < a.n_groups;
+    const int hg = (int)stream % a.hgroups;
+    kvh = (int)stream / a.hgroups;
     // tiles in the sequence's numbering; groups of the call, longest first
     const int t_end = a.tile0 + a.n_tiles - 1;
-    const int t0 = (t_end / TPG - u / a.n_kv_heads) * TPG;
+    const int t0 = (t_end / TPG - (int)min(group, (long)a.n_groups - 1)) * TPG;
     const int ta = max(t0, a.tile0), tz = min(t0 + TPG - 1, t_end);  // the group's tiles in the call
     const int tt = t0 + wave / WPG;
     wave_ok = tt >= ta && tt <= tz;
@@ -440,7 +451,7 @@ struct Work {
     m_late = (tb.n_sink + qt - tb.win_start) >> 2;
     page_bytes = (uint32_t)(kPage * a.n_kv_heads * kHeadDim);
     scale_stride = (uint32_t)(kPage * a.n_kv_heads);
-    make_plan<4>(plan, a, kvh, wave, lane);
+    make_plan(plan, a, kvh, wave, lane);
   }
   // Q codes of this lane's row for heads hd0 .. in the B-operand layout (16
   // channels per chunk) and rowf = q_scale * softmax_scale * log2(e); rows
@@ -454,12 +465,12 @@ struct Work {
     for (int h = 0; h < H; ++h) {
       const long row = (long)tq * a.n_q_heads + hd0 + h;
       if (QS == QSrc::kBf16) {
-        const uint4* qrow = reinterpret_cast<const uint4*>(a.q_bf16 + row * kHeadDim + 16 * rc.g);
-        uint4 raw[4][2];
+        const v4i* qrow = reinterpret_cast<const v4i*>(a.q_bf16 + row * kHeadDim + 16 * rc.g);
+        v4i raw[4][2];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          raw[c][0] = qrow[8 * c];
-          raw[c][1] = qrow[8 * c + 1];
+          raw[c][0] = __builtin_nontemporal_load(qrow + 8 * c);  // read once: keep it out of L2's way
+          raw[c][1] = __builtin_nontemporal_load(qrow + 8 * c + 1);
         }
         // |x| of finite values ordered as the unsigned magnitude bits; the
         // packed words stay in registers and are widened only once, below
@@ -468,7 +479,8 @@ struct Work {
         for (int c = 0; c < 4; ++c)
 #pragma unroll
           for (int k = 0; k < 2; ++k) {
-            const uint32_t w[4] = {raw[c][k].x, raw[c][k].y, raw[c][k].z, raw[c][k].w};
+            const uint32_t w[4] = {(uint32_t)raw[c][k][0], (uint32_t)raw[c][k][1], (uint32_t)raw[c][k][2],
+                                   (uint32_t)raw[c][k][3]};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               mlo = max(mlo, w[i] & 0x7fffu);
@@ -485,7 +497,8 @@ struct Work {
           uint32_t cw[4];
 #pragma unroll
           for (int k = 0; k < 2; ++k) {
-            const uint32_t w[4] = {raw[c][k].x, raw[c][k].y, raw[c][k].z, raw[c][k].w};
+            const uint32_t w[4] = {(uint32_t)raw[c][k][0], (uint32_t)raw[c][k][1], (uint32_t)raw[c][k][2],
+                                   (uint32_t)raw[c][k][3]};
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
               const uint32_t lo = w[2 * i], hi = w[2 * i + 1];
@@ -502,7 +515,7 @@ struct Work {
       } else {
         const int8_t* qrow = a.q_i8 + row * kHeadDim + 16 * rc.g;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) qf[h][c] = *reinterpret_cast<const v4i*>(qrow + 64 * c);
+        for (int c = 0; c < 4; ++c) qf[h][c] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(qrow + 64 * c));
         qscale[h] = a.q_scale[row];
         rowf[h] = row_ok ? qscale[h] * a.row_mul : 0.f;
       }
@@ -510,92 +523,96 @@ struct Work {
   }
 };
 
-// The attention: the group's key list walked four pages at a time with K and
-// V staged, the running reference, P codes, digit planes and PV, then the
-// epilogue.  One head per wave (HPW = 1): a wave holding two heads'
-// accumulators runs alone on its SIMD and measured slower than two waves per
-// SIMD.
+// The attention: the group's key list walked four pages at a time through
+// the LDS ring, the running reference, P codes, digit planes and PV, then the
+// epilogue.  One head per wave: a wave holding two heads' accumulators would
+// run alone on its SIMD.
 template <int WPG, bool OUT_BF16, bool QF>
-__global__ __launch_bounds__(256, 2) void prefill_attn_kernel(AttnArgs a, const int32_t* __restrict__ pt_arg) {
+__global__ __launch_bounds__(512, 1) void prefill_attn_kernel(AttnArgs a, const int32_t* __restrict__ pt_arg) {
   constexpr int HPW = 1;
-  __shared__ Stage st[2];
+  __shared__ Stage st[kStages];
   const WPA_CONST int32_t* pt = (const WPA_CONST int32_t*)pt_arg;
   Work<WPG> w(a);
-  issue_stage<4, true>(st[0], a, w.plan, w.page_bytes, w.scale_stride, wave_pages<4>(pt, w.tb, 0, w.wave), w.wave);
+  if (!w.valid) return;  // uniform over the workgroup, before any copy or barrier
+  const uint32_t ring = lds_addr(&st[0]);
+  // the first kLead steps' copies, then Q; the wait for Q also covers them
+#pragma unroll
+  for (int i = 0; i < kLead; ++i)
+    if (i < w.n_st)
+      issue_copies(ring + i * sizeof(Stage), a, w.plan, w.page_bytes, w.scale_stride,
+                   step_page(pt, w.tb, i, w.plan.page));
   v4i qf[HPW][4];
-  float rowf[HPW], zref[HPW], lsum[HPW];
-  float qscale[HPW];
+  float rowf[HPW], qscale[HPW];
   w.template load_q<HPW, QF ? QSrc::kBf16 : QSrc::kInt8>(a, w.head0, qf, rowf, qscale);
   // rows past the end read the last token with rowf = 0; their results stay
   // in their own accumulator rows and are never stored
-#pragma unroll
-  for (int h = 0; h < HPW; ++h) {
-    zref[h] = -INFINITY;  // raised by the first step
-    lsum[h] = 0.f;
-  }
-  wait_vmem();
-  // page ids two steps ahead: a scalar load still in flight holds up the
-  // step's first LDS wait (both count on lgkmcnt), so it must be issued early
-  // enough to have returned; entries past the list clamp to its last page
-  WavePages<4> pg1 = wave_pages<4>(pt, w.tb, 1, w.wave), pg2 = wave_pages<4>(pt, w.tb, 2, w.wave);
+  float zref = -INFINITY;  // raised by the first step
+  float lsum = 0.f;
+  wait_vm<0>();
+  // page ids two steps before their copies are issued: a scalar load still
+  // in flight holds up the step's first LDS wait (both count on lgkmcnt), so
+  // it must be issued early enough to have returned
+  int pg1 = step_page(pt, w.tb, kLead, w.plan.page), pg2 = step_page(pt, w.tb, kLead + 1, w.plan.page);
 
-  v4i acc[HPW][2][16];
+  v4i acc[2][16];
 #pragma unroll
-  for (int h = 0; h < HPW; ++h)
+  for (int pl = 0; pl < 2; ++pl)
 #pragma unroll
-    for (int pl = 0; pl < 2; ++pl)
-#pragma unroll
-      for (int nt = 0; nt < 16; ++nt) acc[h][pl][nt] = v4i{0, 0, 0, 0};
-  int buf = 0;
+    for (int nt = 0; nt < 16; ++nt) acc[pl][nt] = v4i{0, 0, 0, 0};
   // every wave runs n_st steps with one barrier each; only which steps are
-  // masked differs between the waves
+  // masked differs between the waves.  Before step `it`, the wave's own
+  // copies of that step are complete once at most the copies of the later
+  // steps already issued (up to kLead - 1 of them) are in flight; the
+  // barrier then makes every wave's copies visible and frees the stage read
+  // in the previous step, which takes the copies kLead steps ahead.
+  static_assert(kLead == 3, "the waits below count two later steps");
   auto next_stage = [&](int it) {
-    wait_stage();
+    const int later = w.n_st - 1 - it;
+    if (later >= 2) wait_vm<2 * kCopies>();
+    else if (later == 1) wait_vm<kCopies>();
+    else wait_vm<0>();
     __syncthreads();
-    if (it + 1 < w.n_st) issue_stage<4, true>(st[buf ^ 1], a, w.plan, w.page_bytes, w.scale_stride, pg1, w.wave);
+    if (it + kLead < w.n_st)
+      issue_copies(ring + ((it + kLead) % kStages) * sizeof(Stage), a, w.plan, w.page_bytes, w.scale_stride, pg1);
     pg1 = pg2;
-    pg2 = wave_pages<4>(pt, w.tb, it + 3, w.wave);
+    pg2 = step_page(pt, w.tb, it + kLead + 2, w.plan.page);
   };
   int it = 0;
   for (; it < min(w.m_early, w.n_st); ++it) {
     next_stage(it);
-    attn_step<HPW, true>(st[buf], qf, w.lane, w.rc.g, rowf, key_mask(w.tb, w.tw, it, w.rc), zref, lsum, acc);
-    buf ^= 1;
+    attn_step<true>(st[it % kStages], qf[0], w.lane, w.rc.g, rowf[0], key_mask(w.tb, w.tw, it, w.rc), zref, lsum,
+                    acc);
   }
   for (; it < w.m_late; ++it) {
     next_stage(it);
-    attn_step<HPW, false>(st[buf], qf, w.lane, w.rc.g, rowf, 0u, zref, lsum, acc);
-    buf ^= 1;
+    attn_step<false>(st[it % kStages], qf[0], w.lane, w.rc.g, rowf[0], 0u, zref, lsum, acc);
   }
   for (; it < w.n_st; ++it) {
     next_stage(it);
-    attn_step<HPW, true>(st[buf], qf, w.lane, w.rc.g, rowf, key_mask(w.tb, w.tw, it, w.rc), zref, lsum, acc);
-    buf ^= 1;
+    attn_step<true>(st[it % kStages], qf[0], w.lane, w.rc.g, rowf[0], key_mask(w.tb, w.tw, it, w.rc), zref, lsum,
+                    acc);
   }
 
   // ---- epilogue: recombine the digit planes, scale by cap / (Xmax * l), store.
   // Output register i of tile nt is row 4g + i, channel 16nt + lane%16.
+  const float rscale = kCap / (kXmax * rows_sum(lsum));
 #pragma unroll
-  for (int h = 0; h < HPW; ++h) {
-    const float rscale = kCap / (kXmax * rows_sum(lsum[h]));
+  for (int i = 0; i < 4; ++i) {
+    const int r = 4 * w.rc.g + i;
+    const float rr = __shfl(rscale, r);
+    const int t = w.qt_local * kPage + r;
+    if (!w.wave_ok || t >= a.n_tokens) continue;
+    const long base = ((long)t * a.n_q_heads + w.head0) * kHeadDim + (w.lane & 15);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 4 * w.rc.g + i;
-      const float rr = __shfl(rscale, r);
-      const int t = w.qt_local * kPage + r;
-      if (!w.wave_ok || t >= a.n_tokens) continue;
-      const long base = ((long)t * a.n_q_heads + w.head0 + h) * kHeadDim + (w.lane & 15);
-#pragma unroll
-      for (int nt = 0; nt < 16; ++nt) {
-        const float x = fmaf((float)acc[h][1][nt][i], 256.f, (float)acc[h][0][nt][i]);
-        const float o = x * rr;
-        if (OUT_BF16) {
-          const uint32_t u32 = __float_as_uint(o);  // round to nearest even
-          const uint16_t hb = (uint16_t)((u32 + 0x7fffu + ((u32 >> 16) & 1u)) >> 16);
-          reinterpret_cast<uint16_t*>(a.out)[base + 16 * nt] = hb;
-        } else {
-          reinterpret_cast<float*>(a.out)[base + 16 * nt] = o;
-        }
+    for (int nt = 0; nt < 16; ++nt) {
+      const float x = fmaf((float)acc[1][nt][i], 256.f, (float)acc[0][nt][i]);
+      const float o = x * rr;
+      if (OUT_BF16) {
+        const uint32_t u32 = __float_as_uint(o);  // round to nearest even
+        const uint16_t hb = (uint16_t)((u32 + 0x7fffu + ((u32 >> 16) & 1u)) >> 16);
+        __builtin_nontemporal_store(hb, reinterpret_cast<uint16_t*>(a.out) + base + 16 * nt);
+      } else {
+        __builtin_nontemporal_store(o, reinterpret_cast<float*>(a.out) + base + 16 * nt);
       }
     }
   }
@@ -603,7 +620,8 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(AttnArgs a, const 
 
 template <int WPG, bool OUT_BF16, bool QF>
 static void launch_wpg(const AttnArgs& a, unsigned grid, hipStream_t stream) {
-  hipLaunchKernelGGL((prefill_attn_kernel<WPG, OUT_BF16, QF>), dim3(grid), dim3(256), 0, stream, a, a.page_table);
+  hipLaunchKernelGGL((prefill_attn_kernel<WPG, OUT_BF16, QF>), dim3(grid), dim3(64 * kWaves), 0, stream, a,
+                     a.page_table);
 }
 template <int WPG>
 static void launch_wpg(const AttnArgs& a, bool out_bf16, unsigned grid, hipStream_t stream) {
@@ -627,6 +645,10 @@ hipError_t launch_prefill_attn(const AttnArgs& args_in, bool out_bf16, hipStream
   // chunk's tiles fall in the same groups as in a whole-sequence call
   const PrefillGrid pg = prefill_grid(a.n_q_heads, a.n_kv_heads, a.tile0, a.n_tiles);
   a.hgroups = pg.hgroups;
+  a.n_groups = (int)pg.n_groups;
+  a.streams = pg.streams;
+  a.xcd_r = pg.xcd_r;
+  a.xcd_q = pg.xcd_q;
   const unsigned grid = (unsigned)pg.workgroups;
   if (pg.wpg == 4) launch_wpg<4>(a, out_bf16, grid, stream);
   else if (pg.wpg == 2) launch_wpg<2>(a, out_bf16, grid, stream);

@@ -24,6 +24,7 @@ struct AttnArgs {
   int q_start;  // sequence position of the call's first query row, a multiple of 16
   // filled in by the launcher
   int G, hgroups, n_tiles, tile0;
+  int n_groups, streams, xcd_r, xcd_q;
   float row_mul;
 };
 
@@ -61,23 +62,53 @@ hipError_t launch_mask_counts(int q_start, int n_tokens, int window_blocks, int 
 // q_bf16 set: the kernels quantize Q as they load it (q_i8, q_scale unused).
 hipError_t launch_prefill_attn(const AttnArgs& args, bool out_bf16, hipStream_t stream);
 
-// Work decomposition of the prefill attention: a workgroup takes wpg query
-// heads of one KV head (the largest of 4, 2, 1 dividing G) on 4/wpg
-// consecutive query tiles, the groups of tiles counted from the sequence's
-// first tile.  Workgroups of a call whose rows start at tile tile0:
+// Work decomposition of the prefill attention: a workgroup (eight waves)
+// takes wpg query heads of one KV head (the largest of 4, 2, 1 dividing G)
+// on 8/wpg consecutive query tiles, the groups of tiles counted from the sequence's
+// first tile.  A stream is one (KV head, head group) pair; its groups are
+// numbered from the last (longest key list) down.
+//
+// Workgroups are dispatched to the chip's eight XCDs in turn (workgroup b
+// runs on XCD b % 8), and each XCD has its own L2.  The order below keeps
+// each stream's consecutive tile groups on as few XCDs as possible, so the
+// key pages a window shares between neighbouring tiles stay in one L2:
+//   * streams dividing 8 (xcd_r = 8 / streams XCDs per stream): XCD x takes
+//     stream x % streams and every xcd_r-th group from x / streams on;
+//   * 8 dividing streams (xcd_q = streams / 8 streams per XCD): XCD x takes
+//     streams x, x + 8, ..., their groups in turn;
+//   * otherwise streams in turn, then groups.
+// Either way each XCD walks its groups longest first.
+constexpr int kXcds = 8;
 struct PrefillGrid {
-  int wpg, tpg, hgroups;
-  long n_groups, workgroups;
+  int wpg, tpg, hgroups, streams, xcd_r, xcd_q;
+  long n_groups, workgroups;  // workgroups launched; the few past the last group exit at once
 };
 inline PrefillGrid prefill_grid(int n_q_heads, int n_kv_heads, int tile0, long n_tiles) {
   PrefillGrid g;
   const int G = n_q_heads / n_kv_heads;
   g.wpg = G % 4 == 0 ? 4 : (G % 2 == 0 ? 2 : 1);
-  g.tpg = 4 / g.wpg;
+  g.tpg = 8 / g.wpg;
   g.hgroups = G / g.wpg;
   g.n_groups = n_tiles > 0 ? (tile0 + n_tiles - 1) / g.tpg - tile0 / g.tpg + 1 : 0;
-  g.workgroups = g.n_groups * n_kv_heads * g.hgroups;
+  g.streams = n_kv_heads * g.hgroups;
+  g.xcd_r = g.streams <= kXcds && kXcds % g.streams == 0 ? kXcds / g.streams : 0;
+  g.xcd_q = g.streams > kXcds && g.streams % kXcds == 0 ? g.streams / kXcds : 0;
+  g.workgroups = g.xcd_r ? kXcds * ((g.n_groups + g.xcd_r - 1) / g.xcd_r) : g.n_groups * g.streams;
   return g;
+}
+// Stream and group (0 = the last, longest) of workgroup b.
+__host__ __device__ inline void prefill_item(long b, int streams, int xcd_r, int xcd_q, long& stream, long& group) {
+  const long x = b % kXcds, j = b / kXcds;
+  if (xcd_r) {
+    stream = x % streams;
+    group = xcd_r * j + x / streams;
+  } else if (xcd_q) {
+    stream = x + kXcds * (j % xcd_q);
+    group = j / xcd_q;
+  } else {
+    stream = b % streams;
+    group = b / streams;
+  }
 }
 
 }  // namespace wpa
