@@ -4,14 +4,16 @@ Each sequence's new token is its last position t = seq_len - 1, attending
 A(t) under the prefill path's mask with the same int8 scheme (int8
 tensor-core prefill attention page, "Why the attention, and why tensor
 cores").  The oracle is therefore the prefill oracle's row t of that sequence
-(workloads.decode_row_case), checked at the same acceptance bars."""
+(workloads.decode_row_case), checked at the same acceptance bars.  Every
+block a query does not attend points at the pool's NaN-scaled page 0, so a
+stray read shows as a non-finite output."""
 import numpy as np
 import pytest
 import torch
 
 import oracle
 import workloads
-from gpu_util import check_parity
+from gpu_util import check_parity, poison_unattended_blocks
 
 pytestmark = pytest.mark.gpu
 
@@ -58,7 +60,7 @@ def check_batch(d, out, label, seqs=None):
     ([64, 400], 10, 2, 0, 0, 58),                          # 5 heads: two row tiles, the second with one head
 ])
 def test_decode_parity(lens, hq, hkv, W, S, seed):
-    d = workloads.make_decode_batch(lens, hq, hkv, W, S, seed=seed)
+    d = poison_unattended_blocks(workloads.make_decode_batch(lens, hq, hkv, W, S, seed=seed))
     dev = upload_batch(d)
     _say(f"decode lens={lens} hq={hq} hkv={hkv} W={W} S={S}")
     o32 = run_decode(d, dev, torch.float32)
@@ -69,7 +71,7 @@ def test_decode_parity(lens, hq, hkv, W, S, seed):
 
 
 def test_decode_zero_and_clamped_lengths():
-    d = workloads.make_decode_batch([200, 100], 8, 2, 4, 1, seed=55, max_blocks=13)
+    d = poison_unattended_blocks(workloads.make_decode_batch([200, 100], 8, 2, 4, 1, seed=55, max_blocks=13))
     dev = upload_batch(d)
     lens = torch.tensor([0, 100000], dtype=torch.int32, device="cuda")  # 0 -> zero row; above the table -> 208
     dev["lens"] = lens
@@ -77,7 +79,8 @@ def test_decode_zero_and_clamped_lengths():
     out = run_decode(d, dev, torch.float32)
     assert torch.all(out[0] == 0)
     d.seq_lens = np.array([1, 13 * 16], dtype=np.int32)
-    d.page_tables[1] = np.random.default_rng(0).permutation(d.k_pool.shape[0])[:13]
+    d.page_tables[1] = np.random.default_rng(0).permutation(d.k_pool.shape[0] - 1)[:13] + 1
+    poison_unattended_blocks(d)
     dev = upload_batch(d)
     dev["lens"] = lens
     out = run_decode(d, dev, torch.float32)
@@ -86,7 +89,7 @@ def test_decode_zero_and_clamped_lengths():
 
 def test_decode_reused_workspace_and_determinism():
     import windowed_int8_paged_amd as wpa
-    d = workloads.make_decode_batch([77, 900, 3000], 8, 2, 16, 1, seed=56)
+    d = poison_unattended_blocks(workloads.make_decode_batch([77, 900, 3000], 8, 2, 16, 1, seed=56))
     dev = upload_batch(d)
     need = wpa.decode_workspace_bytes(3, 8, d.page_tables.shape[1], 16, 1)
     ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")  # NaN-patterned scratch
@@ -99,8 +102,9 @@ def test_decode_reused_workspace_and_determinism():
 
 def test_decode_32k_shape_sampled():
     """The bench shape: every sequence at 32768 tokens, 16 / 4 heads, window 256
-    blocks + 1 sink, each owning the 257 pages it attends; two sequences checked."""
-    d = workloads.make_decode_batch([32768] * 8, 16, 4, 256, 1, seed=57, attended_pages_only=True)
+    blocks + 1 sink, every block on a page of its own, the unattended ones then
+    pointed at the poisoned page; two sequences checked."""
+    d = poison_unattended_blocks(workloads.make_decode_batch([32768] * 8, 16, 4, 256, 1, seed=57, owned_pages=True))
     dev = upload_batch(d)
     _say("decode 32k shape")
     out = run_decode(d, dev, torch.bfloat16)

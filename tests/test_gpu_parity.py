@@ -1,10 +1,11 @@
 """GPU parity: the HIP path through the C ABI against the CPU oracle.
 
 Integer work is bit-exact (Q codes and scales, attended counts); the attention
-output is within max|d| <= 2e-3*max|O| of the int8 mirror and within 3e-2
-relative Frobenius of exact attention.  bf16 outputs are additionally allowed
-half a bf16 ulp, and must equal the round-to-nearest-even of the same kernel's
-fp32 output bit for bit.
+output is within max|d| <= 2e-3*max|O| of the int8 mirror (fp32 outputs with
+no further allowance) and within 3e-2 relative Frobenius of exact attention.
+bf16 outputs are additionally allowed half a bf16 ulp (their own rounding),
+and must equal the round-to-nearest-even of the same kernel's fp32 output bit
+for bit.
 """
 import numpy as np
 import pytest
@@ -12,7 +13,7 @@ import torch
 
 import oracle
 import workloads
-from gpu_util import check_parity, run, upload
+from gpu_util import check_parity, oracle_rows, run, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -118,6 +119,24 @@ def test_outlier_rows_small():
     check_parity(case, o32, label="outliers f32")
 
 
+@pytest.mark.parametrize("scale", [1.0, 4.0])
+def test_peaked_scores(scale):
+    """Strongly peaked softmax rows: a softmax scale 16 and 64 times the
+    default over outlier Q rows (channels x30) and saturated K tokens, so that
+    a few keys carry nearly all of a row's weight and the reference rises by
+    many bits at once.  The kernel is held to the int8 mirror's bar; the
+    method itself (the mirror) is 9% (relative Frobenius) from exact attention
+    on these rows, past the 3e-2 stated for the five workloads, so that
+    comparison is reported, not asserted."""
+    case = workloads.make_case(n_tokens=700, n_q_heads=8, n_kv_heads=2, window_blocks=6, sink_blocks=1,
+                               seed=14, softmax_scale=scale, q_outlier_frac=0.2, k_saturated_frac=0.05,
+                               out_dtype="f32")
+    _say(f"peaked scores, softmax scale {scale}")
+    _, _, o32 = run(case, out_dtype=torch.float32)
+    r = check_parity(case, o32, label=f"peaked x{scale}", frob_bar=None)
+    _say(f"peaked {scale}: {r}")
+
+
 def test_tiny_config_both_containers():
     case = workloads.make_config("tiny")
     dev = upload(case)
@@ -161,24 +180,39 @@ def test_out_of_pool_page_ids_are_clamped():
 
 # ---------------------------------------------------------------- the five workloads, sampled
 
-def sample_tiles(n_tokens, window_blocks):
+def sample_tiles(name, n_tokens, window_blocks, count=32):
+    """The first and last tiles, the middle, the tiles around the window's
+    fill-up, then seeded random tiles up to `count`."""
     nt = (n_tokens + 15) // 16
     tiles = {0, 1, 2, nt // 3, nt // 2, nt - 2, nt - 1}
     if window_blocks > 0:
         tiles |= {window_blocks - 1, window_blocks, window_blocks + 1}
-    return sorted(t for t in tiles if 0 <= t < nt)
+    tiles = {t for t in tiles if 0 <= t < nt}
+    rng = np.random.default_rng(sum(map(ord, name)))
+    while len(tiles) < min(count, nt):
+        tiles.add(int(rng.integers(0, nt)))
+    return sorted(tiles)
 
 
 @pytest.mark.parametrize("name", ["4k", "32k", "64k", "16k_full", "32k_gqa2", "32k_mha"])
 def test_config_sampled_parity(name):
+    """32 tiles per workload (fixed and random ones), in the benchmarked launch
+    (bf16 Q quantized inside the attention, bf16 output), in the separate-quantize
+    launch with bf16 and fp32 output; fp32 meets the plain bar."""
+    import windowed_int8_paged_amd as wpa
     case = workloads.make_config(name)
     dev = upload(case)
-    tiles = sample_tiles(case.n_tokens, case.window_blocks)
-    _say(f"config {name}: tiles {tiles}")
-    _, _, o16 = run(case, dev, out_dtype=torch.bfloat16)        # the benchmarked launch
-    r16 = check_parity(case, o16, tiles=tiles, label=f"{name} bf16")
+    tiles = sample_tiles(name, case.n_tokens, case.window_blocks)
+    _say(f"config {name}: {len(tiles)} tiles {tiles}")
+    _, _, o16 = run(case, dev, out_dtype=torch.bfloat16)
     _, _, o32 = run(case, dev, out_dtype=torch.float32)
-    r32 = check_parity(case, o32, tiles=tiles, label=f"{name} f32")
+    fused = wpa.prefill_attn_fused_q(dev["q_bf16"], dev["k_pool"], dev["v_pool"], dev["k_scale"], dev["v_scale"],
+                                     dev["page_table"], case.window_blocks, case.sink_blocks, case.softmax_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(fused, o16)
     assert torch.equal(o16, o32.to(torch.bfloat16))
     assert torch.isfinite(o16.float()).all()
-    _say(f"config {name}: bf16 {r16} f32 {r32}")
+    ref = oracle_rows(case, tiles)
+    r32 = check_parity(case, o32, tiles=tiles, label=f"{name} f32", ref=ref)
+    r16 = check_parity(case, o16, tiles=tiles, label=f"{name} bf16", ref=ref)
+    _say(f"config {name}: f32 {r32} bf16 {r16}")

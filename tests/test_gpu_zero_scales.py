@@ -87,7 +87,7 @@ def test_prefill_tiny_leading_v_scales():
 def test_decode_zero_v_splits():
     """Whole 8-page splits of zero V (sequence 1's first 800 tokens) and a
     sequence whose every key has zero V (exact zero row)."""
-    d = workloads.make_decode_batch([300, 1500, 200], 8, 2, 0, 0, seed=64, attended_pages_only=True)
+    d = workloads.make_decode_batch([300, 1500, 200], 8, 2, 0, 0, seed=64, owned_pages=True)
     for b, n in ((1, 800), (2, 200)):
         pages = d.page_tables[b, :(n + 15) // 16]
         d.v_pool[pages] = 0

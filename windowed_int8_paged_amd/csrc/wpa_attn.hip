@@ -352,10 +352,14 @@ __device__ inline void attn_step(Stage& st, const v4i (&qf)[4], int lane, int g,
     mx = max(mx, max(max(__float_as_uint(pp[t][0]), __float_as_uint(pp[t][1])),
                      max(__float_as_uint(pp[t][2]), __float_as_uint(pp[t][3]))));
   }
-  // a page whose P' all lie below 2^-60 (masked ones are 0) gets F = 0 and
-  // finite codes, so its weights are exactly zero
-  const float inv = 127.0f * __builtin_amdgcn_rcpf(__uint_as_float(max(mx, __float_as_uint(kTiny))));
-  const uint32_t F = (uint32_t)fmaf(__uint_as_float(mx), kFScale, 0.5f);
+  // inv = 127 / max P' by IEEE division, the method's float32 step.  A page
+  // whose P' all lie below 2^-60 (masked ones are 0) gets F = 0 and finite
+  // codes, so its weights are exactly zero.  F is clamped to 24 bits: P' <= cap
+  // holds only up to the rounding of z, which can pass the cap's margin when
+  // |z| is huge (scores of order 2^13 bits), and a wrapped F would drop the
+  // page's largest weights.
+  const float inv = 127.0f / __uint_as_float(max(mx, __float_as_uint(kTiny)));
+  const uint32_t F = min((uint32_t)fmaf(__uint_as_float(mx), kFScale, 0.5f), 0xFFFFFFu);
   v4i dig[2];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {

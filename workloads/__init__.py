@@ -232,51 +232,40 @@ class DecodeBatch:
 
 
 def make_decode_batch(seq_lens, n_q_heads: int, n_kv_heads: int, window_blocks: int, sink_blocks: int,
-                      seed: int, max_blocks: int | None = None, attended_pages_only: bool = False,
+                      seed: int, max_blocks: int | None = None, owned_pages: bool = False,
                       softmax_scale: float = 1.0 / 16.0) -> DecodeBatch:
     """Seeded decode inputs.  Draw order: Q, pool codes (K, V), scales (K, V), page maps.
 
-    By default every sequence maps its blocks to a seeded random choice of
-    distinct pool pages out of a pool as large as the longest sequence needs
-    (sequences may share pages).  With attended_pages_only, each sequence owns
-    fresh pages for exactly the blocks its last position attends (sink and
-    window blocks) and maps every other block to page 0, which is never read:
-    the whole pool is then what one decode step must stream."""
+    Page 0 of the pool is never mapped and has NaN scales, so that a page
+    table entry pointed at it (as the tests do for blocks a query must not
+    read) poisons any read of it.  By default every sequence maps its blocks
+    to a seeded random choice of distinct pages out of pages 1 .. max_blocks
+    (sequences may share pages).  With owned_pages, every block of every
+    sequence gets a page of its own, so a decode step streams exactly the
+    pages it reads and no two sequences share one."""
     seq_lens = np.asarray(seq_lens, dtype=np.int32)
     batch = len(seq_lens)
     rng = np.random.default_rng(seed)
     need = [(int(L) + PAGE - 1) // PAGE for L in seq_lens]
     max_blocks = max_blocks or max(max(need), 1)
     q = rng.standard_normal((batch, n_q_heads, HEAD_DIM), dtype=np.float32)
-    if attended_pages_only:
-        lists = []
-        for L in seq_lens:
-            t = int(L) - 1
-            qt = t // PAGE
-            if window_blocks <= 0:
-                blocks = list(range(qt + 1))
-            else:
-                rsb = max(0, qt + 1 - window_blocks)
-                blocks = list(range(min(sink_blocks, rsb))) + list(range(rsb, qt + 1))
-            lists.append(blocks)
-        n_pool = 1 + sum(len(b) for b in lists)
-    else:
-        n_pool = max_blocks
+    n_pool = 1 + (sum(need) if owned_pages else max_blocks)
     k_pool = rng.integers(-127, 128, size=(n_pool, PAGE, n_kv_heads, HEAD_DIM), dtype=np.int8)
     v_pool = rng.integers(-127, 128, size=(n_pool, PAGE, n_kv_heads, HEAD_DIM), dtype=np.int8)
     k_scale = rng.uniform(0.005, 0.02, size=(n_pool, PAGE, n_kv_heads)).astype(np.float32)
     v_scale = rng.uniform(0.005, 0.02, size=(n_pool, PAGE, n_kv_heads)).astype(np.float32)
+    k_scale[0] = np.nan
+    v_scale[0] = np.nan
     tables = np.full((batch, max_blocks), -1, dtype=np.int32)
-    if attended_pages_only:
-        nxt = 1
-        for b, blocks in enumerate(lists):
-            tables[b, :need[b]] = 0
-            fresh = rng.permutation(len(blocks)).astype(np.int32) + nxt
-            tables[b, blocks] = fresh
-            nxt += len(blocks)
+    if owned_pages:
+        order = rng.permutation(n_pool - 1).astype(np.int32) + 1
+        nxt = 0
+        for b in range(batch):
+            tables[b, :need[b]] = order[nxt:nxt + need[b]]
+            nxt += need[b]
     else:
         for b in range(batch):
-            tables[b, :need[b]] = rng.permutation(n_pool)[:need[b]]
+            tables[b, :need[b]] = rng.permutation(n_pool - 1)[:need[b]] + 1
     qb = _round_to_bf16_bits(q)
     return DecodeBatch(n_q_heads, n_kv_heads, window_blocks, sink_blocks, softmax_scale, qb,
                        _bf16_bits_to_f32(qb), k_pool, v_pool, k_scale, v_scale, tables, seq_lens)
