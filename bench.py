@@ -80,6 +80,32 @@ def warm_up(step, args) -> None:
         torch.cuda.synchronize()
 
 
+def sample_clock(step):
+    """GFX clock under this load: amd-smi's reading of every XCD's clock,
+    taken while steps run back to back.  Returns MHz (mean over XCDs) or None."""
+    import subprocess
+    import torch
+    try:
+        proc = subprocess.Popen(["amd-smi", "metric", "--clock", "-g", str(torch.cuda.current_device()), "--json"],
+                                stdout=subprocess.PIPE, stderr=subprocess.DEVNULL, text=True)
+    except OSError:
+        return None
+    t0 = time.perf_counter()
+    while proc.poll() is None and time.perf_counter() - t0 < 30:
+        for _ in range(4):
+            step()
+        torch.cuda.synchronize()
+    try:
+        out, _ = proc.communicate(timeout=10)
+        data = json.loads(out)
+        gpu = data["gpu_data"][0] if isinstance(data, dict) else data[0]
+        clocks = [v["clk"]["value"] for k, v in gpu["clock"].items() if k.startswith("gfx_")]
+        clocks = [float(c) for c in clocks if isinstance(c, (int, float))]
+        return sum(clocks) / len(clocks) if clocks else None
+    except Exception:  # no reading: the line carries null
+        return None
+
+
 def blas_threads() -> int:
     """Threads the oracle's numpy BLAS calls run on."""
     try:
@@ -90,7 +116,9 @@ def blas_threads() -> int:
 
 
 def cpu_baseline(case, seconds: float):
-    """Time the oracle's int8 mirror (as it stands) on a bounded sample of tiles."""
+    """Time the oracle (as it stands) on a bounded sample of whole query tiles:
+    the int8 mirror (mode b) for about two thirds of `seconds`, then exact
+    attention (mode a) on the same tiles for the rest."""
     import numpy as np
     import oracle
     threads = blas_threads()
@@ -100,21 +128,36 @@ def cpu_baseline(case, seconds: float):
     first = min(n_tiles - 1, max(0, case.window_blocks + 1)) if case.window_blocks > 0 else n_tiles // 2
     span = n_tiles - first
     order = [first + (7 * i) % span for i in range(span)] if span % 7 else list(range(first, n_tiles))
+
+    def ops_of(tiles):
+        rows = np.concatenate([oracle.tile_rows(case.n_tokens, t) for t in tiles])
+        counts = oracle.mask_counts(case.n_tokens, case.window_blocks, case.sink_blocks)[rows]
+        return rows, counts, 4.0 * counts.sum() * 256 * case.n_q_heads
+
     tiles, t0 = [], time.perf_counter()
     for tile in order:
         oracle.attention_int8_mirror(case, tiles=[tile])
         tiles.append(tile)
-        if time.perf_counter() - t0 >= seconds:
+        if time.perf_counter() - t0 >= seconds * 2 / 3:
             break
-    dt = time.perf_counter() - t0
-    rows = np.concatenate([oracle.tile_rows(case.n_tokens, t) for t in tiles])
-    counts = oracle.mask_counts(case.n_tokens, case.window_blocks, case.sink_blocks)[rows]
-    ops = 4.0 * counts.sum() * 256 * case.n_q_heads
+    dt_b = time.perf_counter() - t0
+    rows, counts, ops_b = ops_of(tiles)
+    tiles_a, t0 = [], time.perf_counter()
+    for tile in tiles:
+        oracle.attention_exact(case, tiles=[tile])
+        tiles_a.append(tile)
+        if time.perf_counter() - t0 >= seconds / 3:
+            break
+    dt_a = time.perf_counter() - t0
+    _, _, ops_a = ops_of(tiles_a)
     return {
-        "value": ops / dt / 1e12, "unit": "TOPS", "cores": int(threads), "kind": "oracle",
-        "sample": f"int8-mirror oracle (numpy fp64) on {len(tiles)} of {n_tiles} query tiles "
+        "value": ops_b / dt_b / 1e12, "unit": "TOPS", "cores": int(threads), "kind": "oracle",
+        "sample": f"int8-mirror oracle (mode b, numpy fp64) on {len(tiles)} of {n_tiles} query tiles "
                   f"({len(rows)} rows x {case.n_q_heads} heads, {int(counts.sum())} attended keys/head) "
-                  f"of the same workload, {dt:.1f} s; host cpu_count {os.cpu_count()}",
+                  f"of the same workload, {dt_b:.1f} s; host cpu_count {os.cpu_count()}",
+        "exact_value": ops_a / dt_a / 1e12,
+        "exact_sample": f"exact-attention oracle (mode a, numpy fp64) on {len(tiles_a)} of the same tiles, "
+                        f"{dt_a:.1f} s, same op count per tile",
     }
 
 
@@ -224,7 +267,7 @@ def bench_chunk(args):
                                "16-token pages, bf16 Q and output", "attended_keys": keys, "int8_ops_per_step": ops},
         "kernel_ms": {"quantize_q_rows": round(quant_ms, 4), "prefill_attn_i8_chunk": round(attn_ms, 4)},
         "roofline": {"bound": "mfma", "achieved": round(ops / (attn_ms * 1e-3) / 1e12, 2), "peak": PEAK_INT8_TOPS,
-                     "unit": "TFLOP/s", "frac": round(ops / (attn_ms * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4),
+                     "unit": "TOPS", "frac": round(ops / (attn_ms * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4),
                      "traffic": None, "kernel": "prefill_attn_i8_chunk"},
     }
     if not args.no_cpu_baseline:
@@ -245,8 +288,9 @@ def bench_chunk(args):
 
 def bench_decode(args):
     """Split-KV decode: one new token for each of 64 sequences at position 32767
-    (16 q heads / 4 kv heads, window 256 blocks + 1 sink block), each sequence
-    owning the 257 pages its token attends.  HBM-bound: the roofline is the K
+    (16 q heads / 4 kv heads, window 256 blocks + 1 sink block), every block of
+    every sequence on a page of its own (4.3 GB of pool, of which each step
+    reads the 257 pages per sequence its token attends).  HBM-bound: the roofline is the K
     and V rows plus scales of every attended key (plus Q and out)."""
     import numpy as np
     import torch
@@ -254,7 +298,7 @@ def bench_decode(args):
     import workloads
 
     B, L, hq, hkv, W, S = 64, 32768, 16, 4, 256, 1
-    d = workloads.make_decode_batch([L] * B, hq, hkv, W, S, seed=1007, attended_pages_only=True)
+    d = workloads.make_decode_batch([L] * B, hq, hkv, W, S, seed=1007, owned_pages=True)
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
     q = torch.from_numpy(d.q_bf16.view(np.int16)).cuda().view(torch.bfloat16)
     kp, vp, ks, vs = dev(d.k_pool), dev(d.v_pool), dev(d.k_scale), dev(d.v_scale)
@@ -293,7 +337,7 @@ def bench_decode(args):
         "ms_per_step": round(wall * 1e3 / args.steps, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "int8", "data": "synthetic",
         "config": {"workload": f"decode, {B} sequences at position {L - 1}, {hq} q heads / {hkv} kv heads, window "
-                               f"{W} blocks + {S} sink block, each sequence owning its {keys // 16} attended pages",
+                               f"{W} blocks + {S} sink block, every block on its own page, {keys // 16} pages read per sequence",
                    "attended_keys_per_sequence": keys, "bytes_per_step": nbytes,
                    "tokens_per_s": round(B / (wall / args.steps), 1)},
         "kernel_ms": {"quantize_q_rows": round(quant_ms, 4), "decode_attn_i8": round(dec_ms, 4)},
@@ -439,17 +483,23 @@ def main():
     ops = 4.0 * total_keys * 256 * Hq
     warm_up(main_step, args)
 
-    # the timed steps of the chosen user path, then (untimed for `value`) the
-    # int8-Q attention launch alone, the roofline kernel, and the other path
+    # the timed steps of the chosen user path; then, untimed for `value`, the
+    # GFX clock under the same load, the int8-Q attention launch alone and the
+    # other path
     ms_per_step, (quant_ms, main_attn_ms, mask_ms) = timed(main_step, args.steps)
+    clock_mhz = sample_clock(main_step)
     attn_ms = timed(attn_only, args.steps)[1][1]
     other_ms, (other_quant_ms, other_attn_ms, _) = timed(other_step, args.steps)
     value = ops / (ms_per_step * 1e-3) / 1e12
-    attn_tops = ops / (attn_ms * 1e-3) / 1e12
     if args.q_path == "fused":
         fused_ms, sep_quant_ms = main_attn_ms, other_quant_ms
     else:
         fused_ms, sep_quant_ms = other_attn_ms, quant_ms
+    # the roofline kernel is the attention launch of the timed path, timed by
+    # HIP events on the stream it runs on
+    roof_ms = main_attn_ms
+    roof_kernel = "prefill_attn_fused_q" if args.q_path == "fused" else "prefill_attn_i8"
+    roof_tops = ops / (roof_ms * 1e-3) / 1e12
 
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
@@ -471,9 +521,11 @@ def main():
         "kernel_ms": {"prefill_attn_fused_q": round(fused_ms, 4), "quantize_q_rows": round(sep_quant_ms, 4),
                       "prefill_attn_i8": round(attn_ms, 4), "mask_counts": round(mask_ms, 4)},
         "other_q_path_ms_per_step": round(other_ms, 4),
-        "roofline": {"bound": "mfma", "achieved": round(attn_tops, 2), "peak": PEAK_INT8_TOPS,
-                     "unit": "TFLOP/s", "frac": round(attn_tops / PEAK_INT8_TOPS, 4),
-                     "traffic": traffic, "kernel": "prefill_attn_i8",
+        "roofline": {"bound": "mfma", "achieved": round(roof_tops, 2), "peak": PEAK_INT8_TOPS,
+                     "unit": "TOPS", "frac": round(roof_tops / PEAK_INT8_TOPS, 4),
+                     "traffic": traffic, "kernel": roof_kernel, "kernel_ms": round(roof_ms, 4),
+                     "clock_mhz": round(clock_mhz, 1) if clock_mhz else None,
+                     "frac_at_clock": round(roof_tops / (PEAK_INT8_TOPS * clock_mhz / 2400.0), 4) if clock_mhz else None,
                      "kernel_source_hash": kernel_source_hash()},
     }
     if not args.no_cpu_baseline:

@@ -85,12 +85,15 @@ constexpr float kVsFloor = 0x1p-64f;
 // One stage of the ring: the step's four pages of K and of V (row 16p + s is
 // key s of page p), and their scales: ks[p][s] and vs[p][s] for slot s < 16
 // (each 256-byte copy repeats the page's 16 scales four times), with
-// vs[p][16 + s] then overwritten by log2(v_scale).
+// vs[p][16 + s] then overwritten by log2(v_scale).  The scale rows are 272
+// bytes apart, so that the four lane groups reading the same slots of their
+// four pages hit four different sets of banks.
+constexpr int kScaleRow = 68;  // floats per scale row: 64 copied + 4 of padding
 struct alignas(16) Stage {
   int8_t k[kStage];
   int8_t v[kStage];
-  float ks[4][64];
-  float vs[4][64];
+  float ks[4][kScaleRow];
+  float vs[4][kScaleRow];
 };
 
 // LDS swizzle of the staged tiles: the 16-byte chunk c of row r sits in slot
@@ -158,7 +161,7 @@ __device__ inline void make_plan(DmaPlan& pl, const AttnArgs& a, int kvh, int wa
     pl.voff[j] = (uint32_t)(rr * row_bytes + kvh * kHeadDim + 16 * (s ^ swz_pg(16 * p + rr)));
   }
   pl.lds_rows = (uint32_t)((is_v ? offsetof(Stage, v) : offsetof(Stage, k)) + 16 * p * kHeadDim);
-  pl.lds_sc = (uint32_t)((is_v ? offsetof(Stage, vs) : offsetof(Stage, ks)) + 64 * sizeof(float) * p);
+  pl.lds_sc = (uint32_t)((is_v ? offsetof(Stage, vs) : offsetof(Stage, ks)) + kScaleRow * sizeof(float) * p);
   pl.pool = is_v ? a.v_pool : a.k_pool;
   pl.sptr = (is_v ? a.v_scale : a.k_scale) + s * a.n_kv_heads + kvh;
   pl.page = p;
