@@ -13,9 +13,10 @@
  *   - head_dim is fixed at 256 (WPA_HEAD_DIM); a KV page holds exactly 16
  *     tokens (WPA_PAGE_TOKENS), the page being the block of the mask.
  *   - All pointers are DEVICE pointers on the current HIP device.  The caller
- *     allocates and frees every buffer; the library allocates nothing, keeps no
- *     global state, never synchronizes, and is safe to call from several host
- *     threads.  Work is enqueued on `stream` (0 = the legacy default stream)
+ *     allocates and frees every buffer; the library allocates nothing, never
+ *     synchronizes, and is safe to call from several host threads.  Its only
+ *     state is the fixed scratch buffer of wpa_decode_attn_i8_noalloc (a
+ *     static device array per GPU and its looked-up address).  Work is enqueued on `stream` (0 = the legacy default stream)
  *     and the call returns at once; buffers must stay alive until the stream
  *     has passed the call.  Calls with no work (n_tokens == 0) return WPA_OK
  *     and enqueue nothing.
@@ -46,7 +47,8 @@ typedef enum {
   WPA_ERR_NULL = 1,         /* a required pointer is NULL (with n_tokens > 0)          */
   WPA_ERR_SHAPE = 2,        /* a size, count or scale is out of range                  */
   WPA_ERR_UNSUPPORTED = 3,  /* bad dtype, misaligned pointer, or a limit exceeded      */
-  WPA_ERR_LAUNCH = 4        /* the HIP kernel launch failed                            */
+  WPA_ERR_LAUNCH = 4,       /* the HIP kernel launch failed                            */
+  WPA_ERR_TOO_LARGE = 5     /* more scratch needed than WPA_NOALLOC_SCRATCH_BYTES      */
 } wpa_status;
 
 typedef enum { WPA_F32 = 0, WPA_BF16 = 1 } wpa_dtype;
@@ -260,6 +262,28 @@ wpa_status wpa_decode_attn_i8(const int8_t* q_i8, const float* q_scale,
                               int window_blocks, int sink_blocks, float softmax_scale,
                               void* workspace, size_t workspace_bytes,
                               void* out, wpa_dtype out_dtype, hipStream_t stream);
+
+/*
+ * wpa_decode_attn_i8 without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  The split rows go to a fixed buffer of
+ * WPA_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on
+ * until the process ends; its device address is looked up on the first call
+ * on a device (with that device current), and the call allocates nothing.
+ * Arguments, output and errors are those of wpa_decode_attn_i8; a call whose
+ * wpa_decode_workspace_bytes(...) exceeds the buffer returns
+ * WPA_ERR_TOO_LARGE before touching the device.  Every call on one GPU uses
+ * the same buffer (its contents on entry do not matter): calls that overlap
+ * on one GPU, e.g. on two streams, race, and must be ordered by the caller.
+ */
+#define WPA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+wpa_status wpa_decode_attn_i8_noalloc(const int8_t* q_i8, const float* q_scale,
+                                      const int8_t* k_pool, const int8_t* v_pool,
+                                      const float* k_scale, const float* v_scale, int n_pool_pages,
+                                      const int32_t* page_tables, int max_blocks, const int32_t* seq_lens,
+                                      int batch, int n_q_heads, int n_kv_heads,
+                                      int window_blocks, int sink_blocks, float softmax_scale,
+                                      void* out, wpa_dtype out_dtype, hipStream_t stream);
 
 /* Static, human-readable name of a status ("WPA_OK", ...; "unknown status"). */
 const char* wpa_status_string(wpa_status s);

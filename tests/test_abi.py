@@ -46,7 +46,8 @@ def test_header_declares_the_entry_points():
     fns = declared_functions()
     for f in ("wpa_quantize_q_rows", "wpa_prefill_attn_i8", "wpa_mask_counts", "wpa_kv_write_i8",
               "wpa_prefill_attn_i8_chunk", "wpa_mask_counts_chunk", "wpa_decode_attn_i8",
-              "wpa_decode_workspace_bytes", "wpa_prefill_attn_fused_q", "wpa_status_string"):
+              "wpa_decode_workspace_bytes", "wpa_prefill_attn_fused_q", "wpa_decode_attn_i8_noalloc",
+              "wpa_status_string"):
         assert f in fns
 
 
@@ -57,7 +58,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_status_strings(lib):
     assert lib.wpa_status_string(0) == b"WPA_OK"
-    for s in (1, 2, 3, 4):
+    for s in (1, 2, 3, 4, 5):
         assert lib.wpa_status_string(s).startswith(b"WPA_ERR")
     assert lib.wpa_status_string(99) == b"unknown status"
 
@@ -211,6 +212,35 @@ def test_decode_rejects_invalid_arguments(lib):
     assert d(ws=None) == NULL
     assert d(ws=ctypes.c_void_p(0x100004)) == UNSUP
     assert d(batch=0, q=None, lens=None, ws=None, out=None) == OK
+
+
+def test_decode_noalloc_rejects_invalid_arguments(lib):
+    """The no-allocation decode: the workspace checks are replaced by the fixed
+    buffer's size limit, checked on the host before any HIP call."""
+    TOO_LARGE = 5
+
+    def d(q=P, n_pool=4, pt=P, max_blocks=10, lens=P, batch=2, hq=8, hkv=2, W=4, S=1, scale=0.0625, out=P,
+          dtype=1):
+        return lib.wpa_decode_attn_i8_noalloc(q, P, P, P, P, P, n_pool, pt, max_blocks, lens, batch, hq, hkv, W, S,
+                                              scale, out, dtype, None)
+    lib.wpa_decode_attn_i8_noalloc.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
+                                                                        ctypes.c_void_p] + [ctypes.c_int] * 5 + [
+        ctypes.c_float, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    lib.wpa_decode_attn_i8_noalloc.restype = ctypes.c_int
+    assert d(batch=-1) == SHAPE
+    assert d(hq=6, hkv=4) == SHAPE
+    assert d(scale=float("nan")) == SHAPE
+    assert d(dtype=9) == UNSUP
+    assert d(hq=34, hkv=2) == UNSUP
+    assert d(q=None) == NULL
+    assert d(out=None) == NULL
+    assert d(batch=0, q=None, lens=None, out=None) == OK
+    # one more sequence than the 64 MiB buffer holds (16 heads x 33 splits x 260 floats each)
+    limit = 64 << 20
+    per_seq = lib.wpa_decode_workspace_bytes(1, 16, 2048, 256, 1)
+    fit = limit // per_seq
+    assert d(batch=fit + 1, hq=16, hkv=4, max_blocks=2048, W=256, S=1) == TOO_LARGE
+    assert lib.wpa_status_string(TOO_LARGE).startswith(b"WPA_ERR_TOO_LARGE")
 
 
 def test_host_block_list_matches_oracle_counts():

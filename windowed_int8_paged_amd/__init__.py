@@ -17,6 +17,8 @@ Entry points mirror the C ABI in include/wpa.h:
     decode_attn_i8(q_i8, q_scale, k_pool, v_pool, k_scale, v_scale, page_tables, seq_lens,
                    window_blocks, sink_blocks, softmax_scale, out=None, out_dtype=torch.bfloat16,
                    workspace=None)                     -> out
+    decode_attn_i8_noalloc(...same as decode_attn_i8 without workspace...) -> out
+                                                       (the library's fixed scratch; nothing allocated by the call)
 """
 from __future__ import annotations
 
@@ -27,11 +29,13 @@ import torch
 
 __all__ = ["quantize_q_rows", "prefill_attn_i8", "prefill_attn_i8_chunk", "prefill_attn_fused_q", "mask_counts",
            "mask_counts_chunk",
-           "kv_write_i8", "decode_attn_i8", "decode_workspace_bytes", "lib", "LIB_PATH",
+           "kv_write_i8", "decode_attn_i8", "decode_attn_i8_noalloc", "decode_workspace_bytes", "NOALLOC_SCRATCH_BYTES",
+           "lib", "LIB_PATH",
            "HEAD_DIM", "PAGE_TOKENS", "WpaError"]
 
 HEAD_DIM = 256
 PAGE_TOKENS = 16
+NOALLOC_SCRATCH_BYTES = 64 << 20  # WPA_NOALLOC_SCRATCH_BYTES
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libwpa.so")
 
 WPA_F32, WPA_BF16 = 0, 1
@@ -63,6 +67,8 @@ def _load():
     L.wpa_decode_attn_i8.argtypes = [vp, vp, vp, vp, vp, vp, ci, vp, ci, vp, ci, ci, ci, ci, ci, cf, vp,
                                      ctypes.c_size_t, vp, ci, vp]
     L.wpa_decode_attn_i8.restype = ci
+    L.wpa_decode_attn_i8_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, ci, vp, ci, vp, ci, ci, ci, ci, ci, cf, vp, ci, vp]
+    L.wpa_decode_attn_i8_noalloc.restype = ci
     L.wpa_kv_write_i8.argtypes = [vp, vp, ci, ci, ci, vp, ci, vp, vp, vp, vp, vp]
     L.wpa_kv_write_i8.restype = ci
     L.wpa_status_string.argtypes = [ci]
@@ -259,3 +265,38 @@ def decode_attn_i8(q_i8, q_scale, k_pool, v_pool, k_scale, v_scale, page_tables,
         float(softmax_scale), _ptr(workspace), workspace.numel(), _ptr(out),
         WPA_BF16 if out.dtype == torch.bfloat16 else WPA_F32, _stream(q_i8.device)))
     return out
+
+
+def decode_attn_i8_noalloc(q_i8, q_scale, k_pool, v_pool, k_scale, v_scale, page_tables, seq_lens,
+                           window_blocks, sink_blocks, softmax_scale, out=None, out_dtype=torch.bfloat16):
+    """decode_attn_i8 with the library's fixed scratch buffer instead of a workspace
+    (wpa_decode_attn_i8_noalloc; see include/wpa.h).  Calls on one GPU share that
+    buffer, so calls that overlap on one GPU race."""
+    _dev(q_i8, "q_i8", torch.int8)
+    batch, hq, d = q_i8.shape
+    if d != HEAD_DIM:
+        raise ValueError("head_dim must be 256")
+    _dev(q_scale, "q_scale", torch.float32, (batch, hq))
+    _dev(k_pool, "k_pool", torch.int8)
+    n_pool, page, hkv, d2 = k_pool.shape
+    if page != PAGE_TOKENS or d2 != HEAD_DIM:
+        raise ValueError("pool pages must be [16][n_kv_heads][256]")
+    _dev(v_pool, "v_pool", torch.int8, k_pool.shape)
+    _dev(k_scale, "k_scale", torch.float32, (n_pool, page, hkv))
+    _dev(v_scale, "v_scale", torch.float32, (n_pool, page, hkv))
+    _dev(page_tables, "page_tables", torch.int32)
+    if page_tables.dim() != 2 or page_tables.shape[0] != batch:
+        raise ValueError("page_tables must be [batch][max_blocks]")
+    _dev(seq_lens, "seq_lens", torch.int32, (batch,))
+    if out is None:
+        out = torch.empty((batch, hq, d), dtype=out_dtype, device=q_i8.device)
+    if out.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("out must be bfloat16 or float32")
+    _dev(out, "out", out.dtype, (batch, hq, d))
+    _check(lib.wpa_decode_attn_i8_noalloc(
+        _ptr(q_i8), _ptr(q_scale), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale), n_pool,
+        _ptr(page_tables), page_tables.shape[1], _ptr(seq_lens), batch, hq, hkv, int(window_blocks),
+        int(sink_blocks), float(softmax_scale), _ptr(out), WPA_BF16 if out.dtype == torch.bfloat16 else WPA_F32,
+        _stream(q_i8.device)))
+    return out
+

@@ -33,6 +33,8 @@ const char* wpa_status_string(wpa_status s) {
     case WPA_ERR_SHAPE: return "WPA_ERR_SHAPE: a size, count or scale is out of range";
     case WPA_ERR_UNSUPPORTED: return "WPA_ERR_UNSUPPORTED: dtype, alignment or a size limit";
     case WPA_ERR_LAUNCH: return "WPA_ERR_LAUNCH: the HIP kernel launch failed";
+    case WPA_ERR_TOO_LARGE:
+      return "WPA_ERR_TOO_LARGE: the call needs more scratch than the fixed buffer holds (WPA_NOALLOC_SCRATCH_BYTES)";
   }
   return "unknown status";
 }
@@ -174,28 +176,37 @@ size_t wpa_decode_workspace_bytes(int batch, int n_q_heads, int max_blocks, int 
   return (size_t)batch * n_q_heads * splits * wpa::kWsRow * sizeof(float);
 }
 
-wpa_status wpa_decode_attn_i8(const int8_t* q_i8, const float* q_scale, const int8_t* k_pool, const int8_t* v_pool,
-                              const float* k_scale, const float* v_scale, int n_pool_pages,
-                              const int32_t* page_tables, int max_blocks, const int32_t* seq_lens, int batch,
-                              int n_q_heads, int n_kv_heads, int window_blocks, int sink_blocks, float softmax_scale,
-                              void* workspace, size_t workspace_bytes, void* out, wpa_dtype out_dtype,
-                              hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Host checks shared by the two decode entry points (all but the workspace).
+wpa_status decode_check(const int8_t* q_i8, const float* q_scale, const int8_t* k_pool, const int8_t* v_pool,
+                        const float* k_scale, const float* v_scale, int n_pool_pages, const int32_t* page_tables,
+                        int max_blocks, const int32_t* seq_lens, int batch, int n_q_heads, int n_kv_heads,
+                        int window_blocks, int sink_blocks, float softmax_scale, const void* out,
+                        wpa_dtype out_dtype) {
   if (batch < 0 || n_q_heads <= 0 || n_kv_heads <= 0 || n_q_heads % n_kv_heads != 0) return WPA_ERR_SHAPE;
   if (max_blocks <= 0 || n_pool_pages <= 0 || sink_blocks < 0) return WPA_ERR_SHAPE;
   if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return WPA_ERR_SHAPE;
   if (out_dtype != WPA_BF16 && out_dtype != WPA_F32) return WPA_ERR_UNSUPPORTED;
   if (n_q_heads / n_kv_heads > wpa::kMaxDecodeG) return WPA_ERR_UNSUPPORTED;
   if (batch == 0) return WPA_OK;
-  if (!q_i8 || !q_scale || !k_pool || !v_pool || !k_scale || !v_scale || !page_tables || !seq_lens || !workspace ||
-      !out)
+  if (!q_i8 || !q_scale || !k_pool || !v_pool || !k_scale || !v_scale || !page_tables || !seq_lens || !out)
     return WPA_ERR_NULL;
-  if (workspace_bytes < wpa_decode_workspace_bytes(batch, n_q_heads, max_blocks, window_blocks, sink_blocks))
-    return WPA_ERR_SHAPE;
-  if (!aligned16(q_i8) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(workspace))
-    return WPA_ERR_UNSUPPORTED;
+  if (!aligned16(q_i8) || !aligned16(k_pool) || !aligned16(v_pool)) return WPA_ERR_UNSUPPORTED;
   const long splits = wpa::decode_splits(max_blocks, window_blocks, sink_blocks);
   if ((long)batch * n_kv_heads * splits > 0x7fffffffL || (long)batch * n_q_heads > 0x7fffffffL)
     return WPA_ERR_UNSUPPORTED;
+  (void)window_blocks;
+  return WPA_OK;
+}
+
+wpa_status decode_launch(const int8_t* q_i8, const float* q_scale, const int8_t* k_pool, const int8_t* v_pool,
+                         const float* k_scale, const float* v_scale, int n_pool_pages, const int32_t* page_tables,
+                         int max_blocks, const int32_t* seq_lens, int batch, int n_q_heads, int n_kv_heads,
+                         int window_blocks, int sink_blocks, float softmax_scale, float* ws, void* out,
+                         wpa_dtype out_dtype, hipStream_t stream) {
   wpa::DecodeArgs a = {};
   a.q_i8 = q_i8;
   a.q_scale = q_scale;
@@ -205,7 +216,7 @@ wpa_status wpa_decode_attn_i8(const int8_t* q_i8, const float* q_scale, const in
   a.v_scale = v_scale;
   a.page_tables = page_tables;
   a.seq_lens = seq_lens;
-  a.ws = static_cast<float*>(workspace);
+  a.ws = ws;
   a.out = out;
   a.n_pool_pages = n_pool_pages;
   a.max_blocks = max_blocks;
@@ -217,6 +228,51 @@ wpa_status wpa_decode_attn_i8(const int8_t* q_i8, const float* q_scale, const in
   a.softmax_scale = softmax_scale;
   if (wpa::launch_decode(a, out_dtype == WPA_BF16, stream) != hipSuccess) return WPA_ERR_LAUNCH;
   return WPA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+wpa_status wpa_decode_attn_i8(const int8_t* q_i8, const float* q_scale, const int8_t* k_pool, const int8_t* v_pool,
+                              const float* k_scale, const float* v_scale, int n_pool_pages,
+                              const int32_t* page_tables, int max_blocks, const int32_t* seq_lens, int batch,
+                              int n_q_heads, int n_kv_heads, int window_blocks, int sink_blocks, float softmax_scale,
+                              void* workspace, size_t workspace_bytes, void* out, wpa_dtype out_dtype,
+                              hipStream_t stream) {
+  const wpa_status st = decode_check(q_i8, q_scale, k_pool, v_pool, k_scale, v_scale, n_pool_pages, page_tables,
+                                     max_blocks, seq_lens, batch, n_q_heads, n_kv_heads, window_blocks, sink_blocks,
+                                     softmax_scale, out, out_dtype);
+  if (st != WPA_OK || batch == 0) return st;
+  if (!workspace) return WPA_ERR_NULL;
+  if (workspace_bytes < wpa_decode_workspace_bytes(batch, n_q_heads, max_blocks, window_blocks, sink_blocks))
+    return WPA_ERR_SHAPE;
+  if (!aligned16(workspace)) return WPA_ERR_UNSUPPORTED;
+  return decode_launch(q_i8, q_scale, k_pool, v_pool, k_scale, v_scale, n_pool_pages, page_tables, max_blocks,
+                       seq_lens, batch, n_q_heads, n_kv_heads, window_blocks, sink_blocks, softmax_scale,
+                       static_cast<float*>(workspace), out, out_dtype, stream);
+}
+
+wpa_status wpa_decode_attn_i8_noalloc(const int8_t* q_i8, const float* q_scale, const int8_t* k_pool,
+                                      const int8_t* v_pool, const float* k_scale, const float* v_scale,
+                                      int n_pool_pages, const int32_t* page_tables, int max_blocks,
+                                      const int32_t* seq_lens, int batch, int n_q_heads, int n_kv_heads,
+                                      int window_blocks, int sink_blocks, float softmax_scale, void* out,
+                                      wpa_dtype out_dtype, hipStream_t stream) {
+  static_assert(WPA_NOALLOC_SCRATCH_BYTES == wpa::kNoAllocScratchBytes, "one stated size");
+  const wpa_status st = decode_check(q_i8, q_scale, k_pool, v_pool, k_scale, v_scale, n_pool_pages, page_tables,
+                                     max_blocks, seq_lens, batch, n_q_heads, n_kv_heads, window_blocks, sink_blocks,
+                                     softmax_scale, out, out_dtype);
+  if (st != WPA_OK || batch == 0) return st;
+  // every check above and this one come before any HIP call
+  if (wpa_decode_workspace_bytes(batch, n_q_heads, max_blocks, window_blocks, sink_blocks) >
+      WPA_NOALLOC_SCRATCH_BYTES)
+    return WPA_ERR_TOO_LARGE;
+  void* ws = nullptr;
+  if (wpa::noalloc_scratch(&ws) != hipSuccess) return WPA_ERR_LAUNCH;
+  return decode_launch(q_i8, q_scale, k_pool, v_pool, k_scale, v_scale, n_pool_pages, page_tables, max_blocks,
+                       seq_lens, batch, n_q_heads, n_kv_heads, window_blocks, sink_blocks, softmax_scale,
+                       static_cast<float*>(ws), out, out_dtype, stream);
 }
 
 wpa_status wpa_mask_counts_chunk(int q_start, int n_tokens, int window_blocks, int sink_blocks, int32_t* counts,

@@ -37,6 +37,8 @@
 #include "wpa_lanes.h"
 #include "wpa_launch.h"
 
+#include <mutex>
+
 namespace wpa {
 
 constexpr int kSplitPages = 8;  // 4 and 16 measured no faster
@@ -302,6 +304,33 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   } else {
     reinterpret_cast<float*>(a.out)[row * kHeadDim + tid] = x;
   }
+}
+
+// ---- The fixed device buffer of wpa_decode_attn_i8_noalloc: the split
+// kernel's partial rows live here instead of in a caller workspace.  In host
+// code `scratch` names a host-side stand-in, not device memory: its device
+// address is looked up once per device with that device current and kept;
+// every launch gets that address.  Every GPU holds its own copy until the
+// process ends; calls on one GPU share it.
+static __device__ __align__(256) float scratch[kNoAllocScratchBytes / sizeof(float)];
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mutex;
+static void* g_scratch_addr[kMaxDevices] = {};
+
+hipError_t noalloc_scratch(void** addr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_addr[dev] = p;
+  }
+  *addr = g_scratch_addr[dev];
+  return hipSuccess;
 }
 
 int decode_splits(int max_blocks, int window_blocks, int sink_blocks) {

@@ -50,6 +50,10 @@ struct DecodeArgs {
   float row_mul;
 };
 int decode_splits(int max_blocks, int window_blocks, int sink_blocks);
+// The decode's fixed scratch for callers that cannot allocate: its size, and
+// its device address on the current device (looked up on first use there).
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+hipError_t noalloc_scratch(void** addr);
 hipError_t launch_decode(const DecodeArgs& args, bool out_bf16, hipStream_t stream);
 
 hipError_t launch_quantize_q_rows(const void* q, bool bf16, int n_tokens, int n_q_heads, int8_t* q_i8,
