@@ -28,7 +28,7 @@ PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 matrix peak, 5.0 POP/s
 HBM_PEAK_GBS = 8000.0
 ATTN_KERNEL_SOURCES = ["windowed_int8_paged_amd/csrc/wpa_attn.hip", "windowed_int8_paged_amd/csrc/wpa_common.h",
                        "windowed_int8_paged_amd/csrc/wpa_lanes.h"]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_prefill_attn_32k.json")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "prefill_attn_32k_counters.json")
 
 
 def kernel_source_hash() -> str:
@@ -78,32 +78,6 @@ def warm_up(step, args) -> None:
         for _ in range(8):
             step()
         torch.cuda.synchronize()
-
-
-def sample_clock(step):
-    """GFX clock under this load: amd-smi's reading of every XCD's clock,
-    taken while steps run back to back.  Returns MHz (mean over XCDs) or None."""
-    import subprocess
-    import torch
-    try:
-        proc = subprocess.Popen(["amd-smi", "metric", "--clock", "-g", str(torch.cuda.current_device()), "--json"],
-                                stdout=subprocess.PIPE, stderr=subprocess.DEVNULL, text=True)
-    except OSError:
-        return None
-    t0 = time.perf_counter()
-    while proc.poll() is None and time.perf_counter() - t0 < 30:
-        for _ in range(4):
-            step()
-        torch.cuda.synchronize()
-    try:
-        out, _ = proc.communicate(timeout=10)
-        data = json.loads(out)
-        gpu = data["gpu_data"][0] if isinstance(data, dict) else data[0]
-        clocks = [v["clk"]["value"] for k, v in gpu["clock"].items() if k.startswith("gfx_")]
-        clocks = [float(c) for c in clocks if isinstance(c, (int, float))]
-        return sum(clocks) / len(clocks) if clocks else None
-    except Exception:  # no reading: the line carries null
-        return None
 
 
 def blas_threads() -> int:
@@ -484,10 +458,8 @@ def main():
     warm_up(main_step, args)
 
     # the timed steps of the chosen user path; then, untimed for `value`, the
-    # GFX clock under the same load, the int8-Q attention launch alone and the
-    # other path
+    # int8-Q attention launch alone and the other path
     ms_per_step, (quant_ms, main_attn_ms, mask_ms) = timed(main_step, args.steps)
-    clock_mhz = sample_clock(main_step)
     attn_ms = timed(attn_only, args.steps)[1][1]
     other_ms, (other_quant_ms, other_attn_ms, _) = timed(other_step, args.steps)
     value = ops / (ms_per_step * 1e-3) / 1e12
@@ -501,11 +473,17 @@ def main():
     roof_kernel = "prefill_attn_fused_q" if args.q_path == "fused" else "prefill_attn_i8"
     roof_tops = ops / (roof_ms * 1e-3) / 1e12
 
-    traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        t = json.load(open(TRAFFIC_FILE))
-        if t.get("kernel_source_hash") == kernel_source_hash() and t.get("config") == args.config:
+    # HBM traffic and the clock under this load come from rocprofv3 counters
+    # of the same kernel code (FETCH_SIZE/WRITE_SIZE scaled by a plain copy;
+    # GRBM_GUI_ACTIVE over the dispatch's duration), recorded with the hash of
+    # the source they were taken on: a changed kernel reports null
+    traffic = clock_mhz = None
+    if os.path.exists(COUNTERS_FILE):
+        t = json.load(open(COUNTERS_FILE))
+        if (t.get("kernel_source_hash") == kernel_source_hash() and t.get("config") == args.config
+                and t.get("kernel") == roof_kernel):
             traffic = t.get("hbm_bytes_per_launch")
+            clock_mhz = t.get("clock_mhz")
 
     res = {
         "metric": METRIC, "value": round(value, 2), "unit": "TOPS", "n_gpus": 1,
@@ -524,7 +502,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(roof_tops, 2), "peak": PEAK_INT8_TOPS,
                      "unit": "TOPS", "frac": round(roof_tops / PEAK_INT8_TOPS, 4),
                      "traffic": traffic, "kernel": roof_kernel, "kernel_ms": round(roof_ms, 4),
-                     "clock_mhz": round(clock_mhz, 1) if clock_mhz else None,
+                     "clock_mhz": round(clock_mhz, 1) if clock_mhz else None, "clock_source": "rocprofv3 counters",
                      "frac_at_clock": round(roof_tops / (PEAK_INT8_TOPS * clock_mhz / 2400.0), 4) if clock_mhz else None,
                      "kernel_source_hash": kernel_source_hash()},
     }

@@ -241,8 +241,9 @@ def make_decode_batch(seq_lens, n_q_heads: int, n_kv_heads: int, window_blocks: 
     read) poisons any read of it.  By default every sequence maps its blocks
     to a seeded random choice of distinct pages out of pages 1 .. max_blocks
     (sequences may share pages).  With owned_pages, every block of every
-    sequence gets a page of its own, so a decode step streams exactly the
-    pages it reads and no two sequences share one."""
+    sequence gets a page of its own, sequence b's pages a contiguous range of
+    the pool in seeded random order (a per-sequence allocator), so a decode
+    step streams exactly the pages it reads and no two sequences share one."""
     seq_lens = np.asarray(seq_lens, dtype=np.int32)
     batch = len(seq_lens)
     rng = np.random.default_rng(seed)
@@ -258,10 +259,9 @@ def make_decode_batch(seq_lens, n_q_heads: int, n_kv_heads: int, window_blocks: 
     v_scale[0] = np.nan
     tables = np.full((batch, max_blocks), -1, dtype=np.int32)
     if owned_pages:
-        order = rng.permutation(n_pool - 1).astype(np.int32) + 1
-        nxt = 0
+        nxt = 1
         for b in range(batch):
-            tables[b, :need[b]] = order[nxt:nxt + need[b]]
+            tables[b, :need[b]] = rng.permutation(need[b]).astype(np.int32) + nxt
             nxt += need[b]
     else:
         for b in range(batch):
