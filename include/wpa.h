@@ -38,9 +38,6 @@ extern "C" {
 
 #define WPA_HEAD_DIM 256
 #define WPA_PAGE_TOKENS 16
-/* Largest number of keys one query row may attend: the int32 PV accumulators
- * (|code| <= 128, |v| <= 127 per key) cannot overflow below this. */
-#define WPA_MAX_KEYS_PER_ROW 131072
 
 typedef enum {
   WPA_OK = 0,
@@ -113,8 +110,8 @@ wpa_status wpa_quantize_q_rows(const void* q, wpa_dtype q_dtype, int n_tokens, i
  * Errors: NULL pointer -> WPA_ERR_NULL; n_tokens < 0, heads <= 0,
  * n_q_heads % n_kv_heads != 0, n_pool_pages < ceil(n_tokens/16),
  * sink_blocks < 0, softmax_scale not finite or <= 0 -> WPA_ERR_SHAPE;
- * other dtype, misalignment, or more than WPA_MAX_KEYS_PER_ROW attended keys
- * per row -> WPA_ERR_UNSUPPORTED.
+ * other dtype or misalignment -> WPA_ERR_UNSUPPORTED.  A row may attend any
+ * number of keys (sequence positions stay below 2^31 - 16).
  */
 wpa_status wpa_prefill_attn_i8(const int8_t* q_i8, const float* q_scale,
                                const int8_t* k_pool, const int8_t* v_pool,

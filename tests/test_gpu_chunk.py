@@ -102,3 +102,35 @@ def test_chunk_past_64k():
     tiles = [q_start // 16, q_start // 16 + 97, (q_start + n) // 16 - 1]
     r = check_parity(case, full_rows(case, q_start, out), tiles=tiles, label="chunk 64k+")
     _say(f"  {r}")
+
+
+def test_chunk_rows_past_133000_keys():
+    """A full-causal 16-row chunk at position 134144: each row attends about
+    134000 keys, every V code is +127, and query head 0 is all zero, so its
+    weights are all at full scale after the first step and the int32 PV
+    planes grow by 127 * 127 per key, past 2^31 after about 133000 keys
+    without the kernel's range guard.  Held to the plain bars on the chunk's
+    tile; the oracle takes about half a minute on it."""
+    from gpu_util import oracle_rows
+    import windowed_int8_paged_amd as wpa
+    n_total, q_rows, hq, hkv = 134160, 16, 4, 1
+    case = workloads.make_long_row_case(n_total, q_rows, hq, hkv, seed=42)
+    q_start = n_total - q_rows
+    _say(f"chunk rows attending {n_total} keys")
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    q = torch.from_numpy(case.q_bf16[q_start:].view(np.int16)).cuda().view(torch.bfloat16)
+    q_i8, q_scale = wpa.quantize_q_rows(q)
+    out = wpa.prefill_attn_i8_chunk(q_start, q_i8, q_scale, t(case.k_pool), t(case.v_pool), t(case.k_scale),
+                                    t(case.v_scale), t(case.page_table), 0, 0, case.softmax_scale,
+                                    out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(o))
+    rows, b, a = oracle_rows(case, [q_start // 16])
+    assert np.array_equal(rows, np.arange(q_start, n_total))
+    mo = np.abs(b).max()
+    rel = np.abs(o - b).max() / mo
+    frob = np.linalg.norm(o - a) / np.linalg.norm(a)
+    _say(f"  rel_mirror {rel:.3e} frob_exact {frob:.3e}")
+    assert rel <= 2e-3
+    assert frob <= 3e-2

@@ -14,14 +14,6 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 long ceil_div(long a, long b) { return (a + b - 1) / b; }
 
-// Largest number of keys any row attends: full causal -> n_tokens; otherwise
-// the last 'window_blocks' blocks plus the sink blocks, capped by n_tokens.
-long max_keys_per_row(long n_tokens, int window_blocks, int sink_blocks) {
-  if (window_blocks <= 0) return n_tokens;
-  const long w = (long)WPA_PAGE_TOKENS * ((long)window_blocks + (long)sink_blocks);
-  return w < n_tokens ? w : n_tokens;
-}
-
 }  // namespace
 
 extern "C" {
@@ -91,7 +83,6 @@ wpa_status prefill_attn(const int8_t* q_i8, const float* q_scale, const uint16_t
   if (!have_q || !k_pool || !v_pool || !k_scale || !v_scale || !page_table || !out) return WPA_ERR_NULL;
   if (!aligned16(q_bf16 ? (const void*)q_bf16 : (const void*)q_i8) || !aligned16(k_pool) || !aligned16(v_pool))
     return WPA_ERR_UNSUPPORTED;
-  if (max_keys_per_row(seq, window_blocks, sink_blocks) > WPA_MAX_KEYS_PER_ROW) return WPA_ERR_UNSUPPORTED;
   const long n_tiles = ceil_div(n_tokens, WPA_PAGE_TOKENS);
   if (wpa::prefill_grid(n_q_heads, n_kv_heads, q_start / WPA_PAGE_TOKENS, n_tiles).workgroups > 0x7fffffffL)
     return WPA_ERR_UNSUPPORTED;

@@ -277,6 +277,40 @@ __device__ inline void shift_planes(v4i (&acc)[2][16], int i, int d) {
   }
 }
 
+// Range guard of the int32 planes, for rows of any length.  A key adds at
+// most 128 * 127 to a plane element, so kGuardSteps steps of 64 keys (plus the
+// few masked steps around them) add less than 2^26.  Every kGuardSteps steps,
+// a row holding a plane element of magnitude 2^30 or more has its reference
+// raised by one bit: its planes are shifted right by one (exactly, as for any
+// raise) and l is halved, so every element stays below 2^31 whatever the
+// row's length.  Accumulator register i of lane (column c, group g) is row
+// 4g + i; the softmax state of row r sits in lanes r, r + 16, r + 32, r + 48.
+constexpr int kGuardSteps = 64;
+__device__ inline void guard_planes(v4i (&acc)[2][16], int lane, float& zref, float& lsum) {
+  uint64_t big[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    int hi = INT32_MIN, lo = INT32_MAX;
+#pragma unroll
+    for (int nt = 0; nt < 16; ++nt)
+#pragma unroll
+      for (int pl = 0; pl < 2; ++pl) {
+        hi = max(hi, acc[pl][nt][i]);
+        lo = min(lo, acc[pl][nt][i]);
+      }
+    big[i] = __builtin_amdgcn_ballot_w64(hi >= (1 << 30) || lo <= -(1 << 30));
+  }
+  if ((big[0] | big[1] | big[2] | big[3]) == 0) return;
+  const int g = lane >> 4, r = lane & 15;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) shift_planes(acc, i, ((big[i] >> (16 * g)) & 0xffffu) ? 1 : 0);
+  const uint64_t mine = big[r & 3] >> (16 * (r >> 2));  // this lane's softmax row r = 4 (r/4) + r%4
+  if (mine & 0xffffu) {
+    zref += 1.f;
+    lsum *= 0.5f;
+  }
+}
+
 // One step of one wave.  z = acc*k_scale*rowf + log2(v_scale) (rowf = q
 // scale * softmax scale * log2 e); the row maximum of z over the step raises
 // the reference zref when it passes it (the accumulators and l of a raised
@@ -593,6 +627,7 @@ __global__ __launch_bounds__(512, 1) void prefill_attn_kernel(AttnArgs a, const 
   for (; it < w.m_late; ++it) {
     next_stage(it);
     attn_step<false>(st[it % kStages], qf[0], w.lane, w.rc.g, rowf[0], 0u, zref, lsum, acc);
+    if (it % kGuardSteps == kGuardSteps - 1) guard_planes(acc, w.lane, zref, lsum);
   }
   for (; it < w.n_st; ++it) {
     next_stage(it);

@@ -30,7 +30,8 @@ import numpy as np
 HEAD_DIM = 256
 PAGE = 16
 
-__all__ = ["Case", "CONFIGS", "make_config", "make_case", "make_kv_rows", "make_decode_batch", "decode_row_case", "HEAD_DIM", "PAGE"]
+__all__ = ["Case", "CONFIGS", "make_config", "make_case", "make_long_row_case", "make_kv_rows", "make_decode_batch",
+           "decode_row_case", "HEAD_DIM", "PAGE"]
 
 
 @dataclasses.dataclass
@@ -185,6 +186,35 @@ def make_config(name: str, seed: int | None = None) -> Case:
     if seed is not None:
         kw["seed"] = seed
     return make_case(name=name, **kw)
+
+
+def make_long_row_case(n_tokens: int, q_rows: int, n_q_heads: int, n_kv_heads: int, seed: int) -> Case:
+    """A full-causal sequence whose last q_rows rows attend n_tokens keys each,
+    with every V code at +127, v_scale 2^-7 on the first 64 tokens and 2^-6
+    on the rest: query head 0 of those rows is all zero, so its scores are all
+    equal and every P * v_scale past the first 64 keys is twice the first
+    ones', which puts the int8 weights at their largest and makes the PV sums
+    grow as fast as they can; the other heads are N(0,1) rounded to bf16.
+    Only the last q_rows rows of Q are drawn; the rest stay zero, and the Q
+    arrays are allocated lazily (np.zeros), so a long sequence costs little
+    memory.  Draw order: Q rows, K codes, k_scale, page permutation."""
+    rng = np.random.default_rng(seed)
+    n_blocks = (n_tokens + PAGE - 1) // PAGE
+    q = rng.standard_normal((q_rows, n_q_heads, HEAD_DIM), dtype=np.float32)
+    q[:, 0] = 0.0
+    k_pool = rng.integers(-127, 128, size=(n_blocks, PAGE, n_kv_heads, HEAD_DIM), dtype=np.int8)
+    k_scale = rng.uniform(0.005, 0.02, size=(n_blocks, PAGE, n_kv_heads)).astype(np.float32)
+    page_table = rng.permutation(n_blocks).astype(np.int32)
+    v_pool = np.full((n_blocks, PAGE, n_kv_heads, HEAD_DIM), 127, dtype=np.int8)
+    v_scale = np.full((n_blocks, PAGE, n_kv_heads), 2.0 ** -6, dtype=np.float32)
+    v_scale[page_table[:4]] = 2.0 ** -7
+    q_bits = np.zeros((n_tokens, n_q_heads, HEAD_DIM), dtype=np.uint16)
+    q_f32 = np.zeros((n_tokens, n_q_heads, HEAD_DIM), dtype=np.float32)
+    q_bits[n_tokens - q_rows:] = _round_to_bf16_bits(q)
+    q_f32[n_tokens - q_rows:] = _bf16_bits_to_f32(q_bits[n_tokens - q_rows:])
+    return Case(name="long_row", n_tokens=n_tokens, n_q_heads=n_q_heads, n_kv_heads=n_kv_heads, window_blocks=0,
+                sink_blocks=0, softmax_scale=1.0 / 16.0, out_dtype="f32", q_bf16=q_bits, q_f32=q_f32,
+                k_pool=k_pool, v_pool=v_pool, k_scale=k_scale, v_scale=v_scale, page_table=page_table, seed=seed)
 
 
 def make_kv_rows(n_tokens: int, n_kv_heads: int, n_pool_pages: int, seed: int):
