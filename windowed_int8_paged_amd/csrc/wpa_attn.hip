@@ -166,17 +166,35 @@ __device__ inline void make_plan(DmaPlan& pl, const AttnArgs& a, int kvh, int wa
   pl.sptr = (is_v ? a.v_scale : a.k_scale) + s * a.n_kv_heads + kvh;
   pl.page = p;
 }
-// The wave's copies of one step into the stage at LDS address `stage`; a
-// page id outside the pool is clamped into it: a wrong page, never memory
+// The copies a wave owes for a later step into the stage at LDS address
+// `stage`.  Inside the loop they are issued one at a time among the current
+// step's PV products rather than in a burst after the barrier: a burst of
+// LDS copies from every wave at once holds up the waves' own operand reads.
+// A page id outside the pool is clamped into it: a wrong page, never memory
 // outside the pool.
-__device__ inline void issue_copies(uint32_t stage, const AttnArgs& a, const DmaPlan& pl, uint32_t page_bytes,
-                                    uint32_t scale_stride, int page_id) {
+struct CopyJob {
+  bool on;              // wave-uniform: is there a step to copy for
+  const int8_t* rows;   // the page's first row in the pool
+  const float* sc;      // this lane's scale source
+  uint32_t lds_rows;    // LDS destinations
+  uint32_t lds_sc;
+};
+__device__ inline CopyJob make_job(bool on, uint32_t stage, const AttnArgs& a, const DmaPlan& pl,
+                                   uint32_t page_bytes, uint32_t scale_stride, int page_id) {
   const uint32_t page = (uint32_t)min(max(page_id, 0), a.n_pool_pages - 1);
-  const uint64_t off = (uint64_t)page * page_bytes;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) dma16(pl.voff[j], pl.pool + off, stage + pl.lds_rows + kKeysPerGroup * kHeadDim * j);
-  dma4(pl.sptr + (uint64_t)page * scale_stride, stage + pl.lds_sc);
+  CopyJob c;
+  c.on = on;
+  c.rows = pl.pool + (uint64_t)page * page_bytes;
+  c.sc = pl.sptr + (uint64_t)page * scale_stride;
+  c.lds_rows = stage + pl.lds_rows;
+  c.lds_sc = stage + pl.lds_sc;
+  return c;
 }
+__device__ inline void copy_part(const CopyJob& c, const DmaPlan& pl, int j) {
+  if (j < 4) dma16(pl.voff[j], c.rows, c.lds_rows + kKeysPerGroup * kHeadDim * j);
+  else dma4(c.sc, c.lds_sc);
+}
+
 // Physical page of list entry 4*step + p, read through the scalar cache;
 // entries past the end clamp to the last one (their keys are masked).
 __device__ inline int step_page(const WPA_CONST int32_t* pt, const TileBlocks& tb, int step, int p) {
@@ -325,7 +343,8 @@ __device__ inline void guard_planes(v4i (&acc)[2][16], int lane, float& zref, fl
 // and 3 of the result are d0 + 128 and d1.
 template <bool MASKED>
 __device__ inline void attn_step(Stage& st, const v4i (&qf)[4], int lane, int g, float rowf, uint32_t kmask,
-                                 float& zref, float& lsum, v4i (&acc)[2][16]) {
+                                 float& zref, float& lsum, v4i (&acc)[2][16], const CopyJob& job,
+                                 const DmaPlan& plan) {
   v4i s[4];
   qk_step<8>(st.k, qf, lane, s);
   // log2(v_scale) of the step's 64 keys, one per lane, into the spare scale
@@ -428,6 +447,7 @@ __device__ inline void attn_step(Stage& st, const v4i (&qf)[4], int lane, int g,
     __builtin_amdgcn_sched_barrier(0);
     acc[0][nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(dig[0], vf[nt], acc[0][nt], 0, 0, 0);
     acc[1][nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(dig[1], vf[nt], acc[1][nt], 0, 0, 0);
+    if (nt % 3 == 2 && job.on) copy_part(job, plan, nt / 3);  // nt = 2, 5, 8, 11, 14: the five copies
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -578,10 +598,13 @@ __global__ __launch_bounds__(512, 1) void prefill_attn_kernel(AttnArgs a, const 
   const uint32_t ring = lds_addr(&st[0]);
   // the first kLead steps' copies, then Q; the wait for Q also covers them
 #pragma unroll
-  for (int i = 0; i < kLead; ++i)
-    if (i < w.n_st)
-      issue_copies(ring + i * sizeof(Stage), a, w.plan, w.page_bytes, w.scale_stride,
-                   step_page(pt, w.tb, i, w.plan.page));
+  for (int i = 0; i < kLead; ++i) {
+    const CopyJob c = make_job(i < w.n_st, ring + i * sizeof(Stage), a, w.plan, w.page_bytes, w.scale_stride,
+                               step_page(pt, w.tb, i, w.plan.page));
+    if (c.on)
+#pragma unroll
+      for (int j = 0; j < kCopies; ++j) copy_part(c, w.plan, j);
+  }
   v4i qf[HPW][4];
   float rowf[HPW], qscale[HPW];
   w.template load_q<HPW, QF ? QSrc::kBf16 : QSrc::kInt8>(a, w.head0, qf, rowf, qscale);
@@ -607,14 +630,15 @@ __global__ __launch_bounds__(512, 1) void prefill_attn_kernel(AttnArgs a, const 
   // barrier then makes every wave's copies visible and frees the stage read
   // in the previous step, which takes the copies kLead steps ahead.
   static_assert(kLead == 3, "the waits below count two later steps");
+  CopyJob job;
   auto next_stage = [&](int it) {
     const int later = w.n_st - 1 - it;
     if (later >= 2) wait_vm<2 * kCopies>();
     else if (later == 1) wait_vm<kCopies>();
     else wait_vm<0>();
     __syncthreads();
-    if (it + kLead < w.n_st)
-      issue_copies(ring + ((it + kLead) % kStages) * sizeof(Stage), a, w.plan, w.page_bytes, w.scale_stride, pg1);
+    job = make_job(it + kLead < w.n_st, ring + ((it + kLead) % kStages) * sizeof(Stage), a, w.plan, w.page_bytes,
+                   w.scale_stride, pg1);
     pg1 = pg2;
     pg2 = step_page(pt, w.tb, it + kLead + 2, w.plan.page);
   };
@@ -622,17 +646,17 @@ __global__ __launch_bounds__(512, 1) void prefill_attn_kernel(AttnArgs a, const 
   for (; it < min(w.m_early, w.n_st); ++it) {
     next_stage(it);
     attn_step<true>(st[it % kStages], qf[0], w.lane, w.rc.g, rowf[0], key_mask(w.tb, w.tw, it, w.rc), zref, lsum,
-                    acc);
+                    acc, job, w.plan);
   }
   for (; it < w.m_late; ++it) {
     next_stage(it);
-    attn_step<false>(st[it % kStages], qf[0], w.lane, w.rc.g, rowf[0], 0u, zref, lsum, acc);
+    attn_step<false>(st[it % kStages], qf[0], w.lane, w.rc.g, rowf[0], 0u, zref, lsum, acc, job, w.plan);
     if (it % kGuardSteps == kGuardSteps - 1) guard_planes(acc, w.lane, zref, lsum);
   }
   for (; it < w.n_st; ++it) {
     next_stage(it);
     attn_step<true>(st[it % kStages], qf[0], w.lane, w.rc.g, rowf[0], key_mask(w.tb, w.tw, it, w.rc), zref, lsum,
-                    acc);
+                    acc, job, w.plan);
   }
 
   // ---- epilogue: recombine the digit planes, scale by cap / (Xmax * l), store.
