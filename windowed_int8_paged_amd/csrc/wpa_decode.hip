@@ -24,7 +24,11 @@
 //     writes it.
 //   * Every load of a split is issued before any is waited on: page ids by
 //     scalar loads, then Q and K straight into matrix-operand registers, V rows
-//     and the scales.  QK^T runs on v_mfma_i32_16x16x64_i8 as S^T = K . Q^T
+//     and the scales.  The V rows are read whole (16 lanes over a key's 256
+//     bytes) as non-temporal loads: read once, whole lines that skip L2
+//     allocation stream faster on this part.  The K operand reads take half a
+//     128-byte line per instruction (the other half comes with the next one),
+//     which needs L2 to keep the line, so they stay ordinary loads.  QK^T runs on v_mfma_i32_16x16x64_i8 as S^T = K . Q^T
 //     (wave w takes pages 2w, 2w+1 of the split; a lane then holds one head
 //     and four keys per page).  PV runs on the same instruction with a block-diagonal P
 //     operand: its 16 rows are (head, page) pairs, row (h, p) holding head
@@ -41,7 +45,7 @@
 
 namespace wpa {
 
-constexpr int kSplitPages = 8;  // 4 and 16 measured no faster
+constexpr int kSplitPages = 8;  // 4 and 16 measured slower
 constexpr int kSplitKeys = kSplitPages * kPage;
 constexpr int kPPW = kSplitPages / 4;  // pages per wave in QK^T and the softmax
 constexpr int kTileKeys = 64;                    // keys of one PV product (four pages)
@@ -112,11 +116,11 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     for (int c = 0; c < 4; ++c) kf[pp][c] = *reinterpret_cast<const v4i*>(krow + 64 * c);
   }
   const int r16 = tid >> 4, c16 = tid & 15;  // V staging: key r16 of each page, 16-byte chunk c16
-  uint4 vv[kSplitPages];
+  v4i vv[kSplitPages];
 #pragma unroll
   for (int p = 0; p < kSplitPages; ++p) {
     const long row = ((long)page[p] * kPage + r16) * a.n_kv_heads + kvh;
-    vv[p] = *reinterpret_cast<const uint4*>(a.v_pool + row * kHeadDim + 16 * c16);
+    vv[p] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(a.v_pool + row * kHeadDim + 16 * c16));
   }
   float ksv = 0.f, vsv = 0.f;
   if (tid < kSplitKeys) {
@@ -127,7 +131,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
   for (int p = 0; p < kSplitPages; ++p) {
     const int key = kPage * (p & 3) + r16;  // key of its 64-key tile
-    *reinterpret_cast<uint4*>(&v_lds[p >> 2][key * kHeadDim + 16 * (c16 ^ swz(key))]) = vv[p];
+    *reinterpret_cast<v4i*>(&v_lds[p >> 2][key * kHeadDim + 16 * (c16 ^ swz(key))]) = vv[p];
   }
   if (tid < kSplitKeys) {
     ks_lds[tid] = ksv;
