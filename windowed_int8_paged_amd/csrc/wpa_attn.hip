@@ -304,6 +304,9 @@ __device__ inline void shift_planes(v4i (&acc)[2][16], int i, int d) {
 // row's length.  Accumulator register i of lane (column c, group g) is row
 // 4g + i; the softmax state of row r sits in lanes r, r + 16, r + 32, r + 48.
 constexpr int kGuardSteps = 64;
+// The fixed cost of a workgroup (Q load, epilogue) in key steps, for
+// balancing the runs of tile groups across XCDs.
+constexpr long kGroupCost = 2;
 __device__ inline void guard_planes(v4i (&acc)[2][16], int lane, float& zref, float& lsum) {
   uint64_t big[4];
 #pragma unroll
@@ -486,7 +489,7 @@ struct Work {
     lane = threadIdx.x & 63;
     wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     long stream, group;
-    prefill_item(blockIdx.x, a.streams, a.xcd_r, a.xcd_q, stream, group);
+    prefill_item(blockIdx.x, a.streams, a.xcd_r, a.xcd_q, a.runs, a.run_start, stream, group);
     valid = group < a.n_groups;
     const int hg = (int)stream % a.hgroups;
     kvh = (int)stream / a.hgroups;
@@ -715,7 +718,33 @@ hipError_t launch_prefill_attn(const AttnArgs& args_in, bool out_bf16, hipStream
   a.streams = pg.streams;
   a.xcd_r = pg.xcd_r;
   a.xcd_q = pg.xcd_q;
-  const unsigned grid = (unsigned)pg.workgroups;
+  long workgroups = pg.workgroups;
+  a.runs = pg.xcd_r && pg.n_groups >= kRunGroups * pg.xcd_r;
+  if (a.runs) {
+    // runs of equal work: group g's key steps (its longest list) plus a fixed
+    // cost, the list as the kernel forms it
+    static_assert(kXcds + 1 <= (int)(sizeof(a.run_start) / sizeof(a.run_start[0])), "run bounds");
+    const int t_end = a.tile0 + a.n_tiles - 1;
+    auto work = [&](long g) {
+      const int t0 = (int)((t_end / pg.tpg - g) * pg.tpg);
+      const int tz = std::min(t0 + pg.tpg - 1, t_end);
+      const TileBlocks tb = tile_blocks(t0, a.window_blocks, a.sink_blocks);
+      return (long)((tb.n_sink + (tz + 1 - tb.win_start) + 3) >> 2) + kGroupCost;
+    };
+    long total = 0;
+    for (long g = 0; g < pg.n_groups; ++g) total += work(g);
+    long acc = 0, g = 0, longest = 0;
+    a.run_start[0] = 0;
+    for (int r = 1; r <= pg.xcd_r; ++r) {
+      const long goal = r == pg.xcd_r ? total : total * r / pg.xcd_r;
+      while (g < pg.n_groups && acc + work(g) <= goal) acc += work(g++);
+      if (r == pg.xcd_r) g = pg.n_groups;
+      a.run_start[r] = (int)g;
+      longest = std::max(longest, (long)(a.run_start[r] - a.run_start[r - 1]));
+    }
+    workgroups = (long)kXcds * longest;
+  }
+  const unsigned grid = (unsigned)workgroups;
   if (pg.wpg == 4) launch_wpg<4>(a, out_bf16, grid, stream);
   else if (pg.wpg == 2) launch_wpg<2>(a, out_bf16, grid, stream);
   else launch_wpg<1>(a, out_bf16, grid, stream);

@@ -25,6 +25,8 @@ struct AttnArgs {
   // filled in by the launcher
   int G, hgroups, n_tiles, tile0;
   int n_groups, streams, xcd_r, xcd_q;
+  int runs;          // with xcd_r: contiguous runs (else every xcd_r-th group)
+  int run_start[9];  // run r holds groups run_start[r] .. run_start[r + 1] - 1
   float row_mul;
 };
 
@@ -77,15 +79,21 @@ hipError_t launch_prefill_attn(const AttnArgs& args, bool out_bf16, hipStream_t 
 // each stream's consecutive tile groups on as few XCDs as possible, so the
 // key pages a window shares between neighbouring tiles stay in one L2:
 //   * streams dividing 8 (xcd_r = 8 / streams XCDs per stream): XCD x takes
-//     stream x % streams and every xcd_r-th group from x / streams on;
+//     stream x % streams.  With many groups (kRunGroups or more per XCD of
+//     the stream), the stream's groups are cut into xcd_r contiguous runs of
+//     equal work (key steps plus a fixed cost per group) and XCD x takes run
+//     x / streams: its L2 then holds one stretch of the sequence.  With few,
+//     it takes every xcd_r-th group from x / streams on, which spreads the
+//     long and short lists evenly over the XCDs;
 //   * 8 dividing streams (xcd_q = streams / 8 streams per XCD): XCD x takes
 //     streams x, x + 8, ..., their groups in turn;
 //   * otherwise streams in turn, then groups.
 // Either way each XCD walks its groups longest first.
 constexpr int kXcds = 8;
+constexpr long kRunGroups = 256;
 struct PrefillGrid {
   int wpg, tpg, hgroups, streams, xcd_r, xcd_q;
-  long n_groups, workgroups;  // workgroups launched; the few past the last group exit at once
+  long n_groups, workgroups;  // workgroups to launch (an upper bound with xcd_r); those past a run exit at once
 };
 inline PrefillGrid prefill_grid(int n_q_heads, int n_kv_heads, int tile0, long n_tiles) {
   PrefillGrid g;
@@ -97,13 +105,23 @@ inline PrefillGrid prefill_grid(int n_q_heads, int n_kv_heads, int tile0, long n
   g.streams = n_kv_heads * g.hgroups;
   g.xcd_r = g.streams <= kXcds && kXcds % g.streams == 0 ? kXcds / g.streams : 0;
   g.xcd_q = g.streams > kXcds && g.streams % kXcds == 0 ? g.streams / kXcds : 0;
-  g.workgroups = g.xcd_r ? kXcds * ((g.n_groups + g.xcd_r - 1) / g.xcd_r) : g.n_groups * g.streams;
+  // with contiguous runs the launcher sizes the grid by its longest run: at most kXcds * n_groups
+  g.workgroups = g.xcd_r ? (g.n_groups >= kRunGroups * g.xcd_r ? kXcds * g.n_groups
+                                                                 : kXcds * ((g.n_groups + g.xcd_r - 1) / g.xcd_r))
+                         : g.n_groups * g.streams;
   return g;
 }
-// Stream and group (0 = the last, longest) of workgroup b.
-__host__ __device__ inline void prefill_item(long b, int streams, int xcd_r, int xcd_q, long& stream, long& group) {
+// Stream and group (0 = the last, longest) of workgroup b; a workgroup past
+// the end of its run gets a group past every run (it exits at once).
+__device__ inline void prefill_item(long b, int streams, int xcd_r, int xcd_q, int runs, const int* run_start,
+                                    long& stream, long& group) {
   const long x = b % kXcds, j = b / kXcds;
-  if (xcd_r) {
+  if (xcd_r && runs) {
+    stream = x % streams;
+    const int r = (int)(x / streams);
+    group = run_start[r] + j;
+    if (group >= run_start[r + 1]) group = 1L << 40;
+  } else if (xcd_r) {
     stream = x % streams;
     group = xcd_r * j + x / streams;
   } else if (xcd_q) {
