@@ -38,9 +38,12 @@
 //   * K and V pages go global -> LDS by asynchronous LDS DMA into row-major
 //     XOR-swizzled tiles, in a ring of four stages filled three steps ahead.
 //     Each wave issues five copies per step (one page of K or of V and its
-//     scales), so a page is fetched once for all eight waves.  LDS fragment
-//     reads are software-pipelined ahead of their matrix products; V operands
-//     are gathered with the transposing read ds_read_b64_tr_b8.
+//     scales), spread among its PV products, so a page is fetched once for
+//     all eight waves.  LDS fragment reads are software-pipelined ahead of
+//     their matrix products; V operands are gathered with the transposing
+//     read ds_read_b64_tr_b8.  The unmasked steps run with their ring stage
+//     known, so every LDS read is a register holding the lane's address plus
+//     an immediate: no address arithmetic in the step.
 //   * From bf16 Q (the fused entry point) each wave quantizes its own rows as
 //     it loads them, by the same formula as the separate quantize kernel.
 
@@ -82,19 +85,24 @@ constexpr float kMaxShift = 2.f * kStageShift;
 // (P' = e * v_scale is unchanged).
 constexpr float kVsFloor = 0x1p-64f;
 
-// One stage of the ring: the step's four pages of K and of V (row 16p + s is
-// key s of page p), and their scales: ks[p][s] and vs[p][s] for slot s < 16
-// (each 256-byte copy repeats the page's 16 scales four times), with
-// vs[p][16 + s] then overwritten by log2(v_scale).  The scale rows are 272
-// bytes apart, so that the four lane groups reading the same slots of their
-// four pages hit four different sets of banks.
-constexpr int kScaleRow = 68;  // floats per scale row: 64 copied + 4 of padding
-struct alignas(16) Stage {
-  int8_t k[kStage];
-  int8_t v[kStage];
-  float ks[4][kScaleRow];
-  float vs[4][kScaleRow];
-};
+// The LDS ring.  Stage s holds the step's four pages of K and of V (row
+// 16p + r is key r of page p) and their scales: ks[p][r] and vs[p][r] for
+// slot r < 16 (each 256-byte copy repeats the page's 16 scales four times),
+// with vs[p][16 + r] then overwritten by log2(v_scale).  The K tiles of the
+// four stages fill the first 64 KB, their V tiles the next 64 KB and the
+// scale rows follow, so a stage's place inside a region fits the 16-bit
+// immediate offset of an LDS read: with the lane's part of every operand
+// address held in a register, a step with a known stage reads LDS with no
+// address arithmetic.  The scale rows are 272 bytes apart, so that the four
+// lane groups reading the same slots of their four pages hit four different
+// sets of banks.
+constexpr int kScaleRow = 68;                                    // floats per scale row: 64 copied + 4 of padding
+constexpr uint32_t kRegionV = kStages * kStage;                  // V tiles
+constexpr uint32_t kRegionSc = 2 * kStages * kStage;             // scale rows
+constexpr uint32_t kScRows = 4 * kScaleRow * sizeof(float);      // the four k (or v) scale rows of a stage
+constexpr uint32_t kScStage = 2 * kScRows;                       // k rows, then v rows
+constexpr uint32_t kLdsBytes = kRegionSc + kStages * kScStage;
+static_assert(kStages * kStage <= 65536, "a stage offset inside a region fits an LDS immediate");
 
 // LDS swizzle of the staged tiles: the 16-byte chunk c of row r sits in slot
 // c ^ swz_pg(r).  The score operand reads (rows 16q + 4t + i, q, i = 0..3, for
@@ -144,8 +152,8 @@ __device__ inline void wait_vm() {
 // copy costs one scalar base per page and no vector arithmetic.
 struct DmaPlan {
   uint32_t voff[4];     // byte offset inside a page, swizzle applied
-  uint32_t lds_rows;    // offset of the wave's page rows inside a stage
-  uint32_t lds_sc;      // offset of the wave's page scales inside a stage
+  uint32_t lds_rows;    // LDS offset of the wave's page rows in stage 0
+  uint32_t lds_sc;      // LDS offset of the wave's page scales in stage 0
   const int8_t* pool;   // k_pool or v_pool
   const float* sptr;    // lane l: the scale of slot l % 16 of page 0
   int page;             // page of the step this wave copies (0..3)
@@ -160,8 +168,8 @@ __device__ inline void make_plan(DmaPlan& pl, const AttnArgs& a, int kvh, int wa
     const int rr = 4 * j + q;  // key inside the page
     pl.voff[j] = (uint32_t)(rr * row_bytes + kvh * kHeadDim + 16 * (s ^ swz_pg(16 * p + rr)));
   }
-  pl.lds_rows = (uint32_t)((is_v ? offsetof(Stage, v) : offsetof(Stage, k)) + 16 * p * kHeadDim);
-  pl.lds_sc = (uint32_t)((is_v ? offsetof(Stage, vs) : offsetof(Stage, ks)) + kScaleRow * sizeof(float) * p);
+  pl.lds_rows = (is_v ? kRegionV : 0u) + (uint32_t)(16 * p * kHeadDim);
+  pl.lds_sc = kRegionSc + (is_v ? kScRows : 0u) + (uint32_t)(kScaleRow * sizeof(float) * p);
   pl.pool = is_v ? a.v_pool : a.k_pool;
   pl.sptr = (is_v ? a.v_scale : a.k_scale) + s * a.n_kv_heads + kvh;
   pl.page = p;
@@ -179,15 +187,15 @@ struct CopyJob {
   uint32_t lds_rows;    // LDS destinations
   uint32_t lds_sc;
 };
-__device__ inline CopyJob make_job(bool on, uint32_t stage, const AttnArgs& a, const DmaPlan& pl,
+__device__ inline CopyJob make_job(bool on, uint32_t ring, int stage, const AttnArgs& a, const DmaPlan& pl,
                                    uint32_t page_bytes, uint32_t scale_stride, int page_id) {
   const uint32_t page = (uint32_t)min(max(page_id, 0), a.n_pool_pages - 1);
   CopyJob c;
   c.on = on;
   c.rows = pl.pool + (uint64_t)page * page_bytes;
   c.sc = pl.sptr + (uint64_t)page * scale_stride;
-  c.lds_rows = stage + pl.lds_rows;
-  c.lds_sc = stage + pl.lds_sc;
+  c.lds_rows = ring + pl.lds_rows + (uint32_t)stage * kStage;
+  c.lds_sc = ring + pl.lds_sc + (uint32_t)stage * kScStage;
   return c;
 }
 __device__ inline void copy_part(const CopyJob& c, const DmaPlan& pl, int j) {
@@ -229,14 +237,51 @@ __device__ inline uint32_t key_mask(const TileBlocks& tb, const TileBlocks& tw, 
 // fences keep the compiler from sinking them back next to their uses (it
 // would otherwise reuse one register set and wait out the full LDS latency
 // before every product).
+// The lane's part of every LDS address a step reads, for stage 0; stage s
+// adds s * kStage (tiles) or s * kScStage (scales), an immediate when s is
+// known.  The values pass through an empty asm so that the compiler keeps
+// them as they are rather than splitting them into a shared base and per-use
+// offsets again.
+struct LdsAddr {
+  uint32_t k[8];   // K fragment of product t, chunk c at k[4 (t % 2) + c], + 2048 for t >= 2
+  uint32_t v[16];  // V operand of column tile nt (keys of the first half; the second is 2048 on)
+  uint32_t ks, vs;   // the lane's page row of k and v scales
+  uint32_t lw, lr;   // log2(v_scale) slot this lane writes, and the v_scale it reads for it
+};
+__device__ inline void make_addr(LdsAddr& A, uint32_t ring, int lane) {
+  const int m = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int r = 16 * (m >> 2) + 4 * t + (m & 3);  // r + 8 (products 2, 3) has the same swizzle
+      A.k[4 * t + c] = ring + (uint32_t)(r * kHeadDim + 16 * ((4 * c + g) ^ swz_pg(r)));
+    }
+  const int key1 = 16 * g + (m >> 1);  // key1 + 8 has the same swizzle
+#pragma unroll
+  for (int nt = 0; nt < 16; ++nt)
+    A.v[nt] = ring + kRegionV + (uint32_t)(key1 * kHeadDim + 8 * (m & 1) + 16 * (nt ^ swz_pg(key1)));
+  A.ks = ring + kRegionSc + (uint32_t)(g * kScaleRow * 4);
+  A.vs = A.ks + kScRows;
+  A.lr = ring + kRegionSc + kScRows + (uint32_t)(g * kScaleRow * 4 + 4 * m);
+  A.lw = A.lr + 16 * 4;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(A.k[i]));
+#pragma unroll
+  for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(A.v[i]));
+  asm volatile("" : "+v"(A.ks), "+v"(A.vs), "+v"(A.lw), "+v"(A.lr));
+}
+typedef float v4f __attribute__((ext_vector_type(4)));  // 16-byte aligned, unlike float4
+template <typename T>
+__device__ inline T lds_read(uint32_t addr) {
+  return *reinterpret_cast<const WPA_LDS T*>((uintptr_t)addr);
+}
+
 template <int D>
-__device__ inline void qk_step(const int8_t* kb, const v4i (&qf)[4], int lane, v4i (&s)[4]) {
-  const int m = lane & 15, kg = lane >> 4;
+__device__ inline void qk_step(const LdsAddr& A, int st, const v4i (&qf)[4], v4i (&s)[4]) {
   auto read = [&](int f) {  // fragment f = 4t + c: product t, channel chunk c
     const int t = f >> 2, c = f & 3;
-    const int r = 16 * (m >> 2) + 4 * t + (m & 3);
-    const int slot = (4 * c + kg) ^ swz_pg(r);
-    return *reinterpret_cast<const v4i*>(kb + r * kHeadDim + 16 * slot);
+    return lds_read<v4i>(A.k[4 * (t & 1) + c] + (uint32_t)(2048 * (t >> 1) + st * kStage));
   };
   v4i kf[16];
 #pragma unroll
@@ -260,22 +305,12 @@ __device__ inline void qk_step(const int8_t* kb, const v4i (&qf)[4], int lane, v
 // transposing read gives lane j byte j%8 of the 8-byte blocks addressed by
 // lanes 2k + j/8 (k = 0..7); lane L here addresses slot L/2 of page g (slot
 // 8 + L/2 in the second read) at channel 16 nt + 8 (L%2).
-struct VFragPg {
-  const int8_t* row1;
-  int sw;
-  __device__ VFragPg(const int8_t* tile, int lane) {
-    const int g = lane >> 4, j = lane & 15;
-    const int key1 = 16 * g + (j >> 1);
-    row1 = tile + key1 * kHeadDim + 8 * (j & 1);
-    sw = swz_pg(key1);  // = swz_pg(key1 + 8)
-  }
-  __device__ v4i operator()(int nt) const {
-    const int8_t* p = row1 + 16 * (nt ^ sw);
-    const v2i lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32((WPA_LDS v2i*)p);
-    const v2i hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32((WPA_LDS v2i*)(p + 8 * kHeadDim));  // key1 + 8
-    return v4i{lo.x, lo.y, hi.x, hi.y};
-  }
-};
+__device__ inline v4i read_v(const LdsAddr& A, int st, int nt) {
+  const uint32_t p = A.v[nt] + (uint32_t)(st * kStage);
+  const v2i lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32(reinterpret_cast<WPA_LDS v2i*>((uintptr_t)p));
+  const v2i hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32(reinterpret_cast<WPA_LDS v2i*>((uintptr_t)(p + 8 * kHeadDim)));
+  return v4i{lo.x, lo.y, hi.x, hi.y};
+}
 
 // Register i of both planes (one accumulator row per 16 lanes) becomes
 // floor((256 hi + lo) / 2^d), exactly, for 0 <= d <= kStageShift: hi keeps
@@ -345,25 +380,27 @@ __device__ inline void guard_planes(v4i (&acc)[2][16], int lane, float& zref, fl
 // by one 24-bit multiply-add; with a bias of 128 in the upper half, bytes 2
 // and 3 of the result are d0 + 128 and d1.
 template <bool MASKED>
-__device__ inline void attn_step(Stage& st, const v4i (&qf)[4], int lane, int g, float rowf, uint32_t kmask,
+__device__ __attribute__((always_inline)) inline void attn_step(const LdsAddr& A, int st, const v4i (&qf)[4], int lane, int g, float rowf, uint32_t kmask,
                                  float& zref, float& lsum, v4i (&acc)[2][16], const CopyJob& job,
                                  const DmaPlan& plan) {
   v4i s[4];
-  qk_step<8>(st.k, qf, lane, s);
+  qk_step<8>(A, st, qf, s);
+  const uint32_t sc = (uint32_t)(st * kScStage);
   // log2(v_scale) of the step's 64 keys, one per lane, into the spare scale
   // slots (every wave writes the same values)
-  st.vs[lane >> 4][16 + (lane & 15)] = __builtin_amdgcn_logf(fmaxf(st.vs[lane >> 4][lane & 15], kVsFloor));
+  *reinterpret_cast<WPA_LDS float*>((uintptr_t)(A.lw + sc)) =
+      __builtin_amdgcn_logf(fmaxf(lds_read<float>(A.lr + sc), kVsFloor));
   __builtin_amdgcn_wave_barrier();
   float sk[4][4];
   float zm = -INFINITY;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    const float4 ks4 = *reinterpret_cast<const float4*>(&st.ks[g][4 * t]);
-    const float4 lv4 = *reinterpret_cast<const float4*>(&st.vs[g][16 + 4 * t]);
+    const v4f ks4 = lds_read<v4f>(A.ks + sc + 16 * t);
+    const v4f lv4 = lds_read<v4f>(A.vs + sc + 64 + 16 * t);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      sk[t][i] = (float)s[t][i] * (&ks4.x)[i];
-      float z = fmaf(sk[t][i], rowf, (&lv4.x)[i]);
+      sk[t][i] = (float)s[t][i] * ks4[i];
+      float z = fmaf(sk[t][i], rowf, lv4[i]);
       if (MASKED) z = ((kmask >> (4 * t + i)) & 1u) ? z : -INFINITY;
       zm = fmaxf(zm, z);
     }
@@ -395,11 +432,11 @@ __device__ inline void attn_step(Stage& st, const v4i (&qf)[4], int lane, int g,
   uint32_t mx = 0;  // bit pattern of the page maximum of P' >= 0
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    const float4 vs4 = *reinterpret_cast<const float4*>(&st.vs[g][4 * t]);
+    const v4f vs4 = lds_read<v4f>(A.vs + sc + 16 * t);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       float e = __builtin_amdgcn_exp2f(fmaf(sk[t][i], rowf, negz));
-      float pv = e * (&vs4.x)[i];
+      float pv = e * vs4[i];
       if (MASKED) {
         const bool ok = (kmask >> (4 * t + i)) & 1u;
         e = ok ? e : 0.f;
@@ -434,19 +471,18 @@ __device__ inline void attn_step(Stage& st, const v4i (&qf)[4], int lane, int g,
     dig[1][t] = (int)__builtin_amdgcn_perm(w23, w01, 0x07050301u);                 // high digit
   }
 
-  // V operand (see VFragPg): reads run two column tiles ahead of their
+  // V operand (see read_v): reads run two column tiles ahead of their
   // products (see qk_step)
   constexpr int DV = 2;
-  const VFragPg read_v(st.v, lane);
   v4i vf[16];
 #pragma unroll
   for (int nt = 0; nt < DV; ++nt) {
-    vf[nt] = read_v(nt);
+    vf[nt] = read_v(A, st, nt);
     __builtin_amdgcn_sched_barrier(0);
   }
 #pragma unroll
   for (int nt = 0; nt < 16; ++nt) {
-    if (nt + DV < 16) vf[nt + DV] = read_v(nt + DV);
+    if (nt + DV < 16) vf[nt + DV] = read_v(A, st, nt + DV);
     __builtin_amdgcn_sched_barrier(0);
     acc[0][nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(dig[0], vf[nt], acc[0][nt], 0, 0, 0);
     acc[1][nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(dig[1], vf[nt], acc[1][nt], 0, 0, 0);
@@ -594,15 +630,15 @@ struct Work {
 template <int WPG, bool OUT_BF16, bool QF>
 __global__ __launch_bounds__(512, 1) void prefill_attn_kernel(AttnArgs a, const int32_t* __restrict__ pt_arg) {
   constexpr int HPW = 1;
-  __shared__ Stage st[kStages];
+  __shared__ alignas(16) int8_t lds[kLdsBytes];
   const WPA_CONST int32_t* pt = (const WPA_CONST int32_t*)pt_arg;
   Work<WPG> w(a);
   if (!w.valid) return;  // uniform over the workgroup, before any copy or barrier
-  const uint32_t ring = lds_addr(&st[0]);
+  const uint32_t ring = lds_addr(&lds[0]);
   // the first kLead steps' copies, then Q; the wait for Q also covers them
 #pragma unroll
   for (int i = 0; i < kLead; ++i) {
-    const CopyJob c = make_job(i < w.n_st, ring + i * sizeof(Stage), a, w.plan, w.page_bytes, w.scale_stride,
+    const CopyJob c = make_job(i < w.n_st, ring, i, a, w.plan, w.page_bytes, w.scale_stride,
                                step_page(pt, w.tb, i, w.plan.page));
     if (c.on)
 #pragma unroll
@@ -621,6 +657,8 @@ __global__ __launch_bounds__(512, 1) void prefill_attn_kernel(AttnArgs a, const 
   // it must be issued early enough to have returned
   int pg1 = step_page(pt, w.tb, kLead, w.plan.page), pg2 = step_page(pt, w.tb, kLead + 1, w.plan.page);
 
+  LdsAddr A;
+  make_addr(A, ring, w.lane);
   v4i acc[2][16];
 #pragma unroll
   for (int pl = 0; pl < 2; ++pl)
@@ -634,33 +672,47 @@ __global__ __launch_bounds__(512, 1) void prefill_attn_kernel(AttnArgs a, const 
   // in the previous step, which takes the copies kLead steps ahead.
   static_assert(kLead == 3, "the waits below count two later steps");
   CopyJob job;
-  auto next_stage = [&](int it) {
+  // `sj` = (it + kLead) % kStages, the stage that takes the copies issued in step it
+  auto next_stage = [&](int it, int sj) __attribute__((always_inline)) {
     const int later = w.n_st - 1 - it;
     if (later >= 2) wait_vm<2 * kCopies>();
     else if (later == 1) wait_vm<kCopies>();
     else wait_vm<0>();
     __syncthreads();
-    job = make_job(it + kLead < w.n_st, ring + ((it + kLead) % kStages) * sizeof(Stage), a, w.plan, w.page_bytes,
-                   w.scale_stride, pg1);
+    job = make_job(it + kLead < w.n_st, ring, sj, a, w.plan, w.page_bytes, w.scale_stride, pg1);
     pg1 = pg2;
     pg2 = step_page(pt, w.tb, it + kLead + 2, w.plan.page);
   };
+  auto plain_step = [&](int it, int st) __attribute__((always_inline)) {
+    next_stage(it, (st + kLead) % kStages);
+    attn_step<false>(A, st, qf[0], w.lane, w.rc.g, rowf[0], 0u, zref, lsum, acc, job, w.plan);
+  };
+  auto masked_step = [&](int it) __attribute__((always_inline)) {
+    next_stage(it, (it + kLead) % kStages);
+    attn_step<true>(A, it % kStages, qf[0], w.lane, w.rc.g, rowf[0], key_mask(w.tb, w.tw, it, w.rc), zref, lsum,
+                    acc, job, w.plan);
+  };
   int it = 0;
-  for (; it < min(w.m_early, w.n_st); ++it) {
-    next_stage(it);
-    attn_step<true>(st[it % kStages], qf[0], w.lane, w.rc.g, rowf[0], key_mask(w.tb, w.tw, it, w.rc), zref, lsum,
-                    acc, job, w.plan);
+  for (; it < min(w.m_early, w.n_st); ++it) masked_step(it);
+  // the unmasked steps lo .. hi-1, with their stages known: the loop walks
+  // the aligned groups of four steps that hold them (step 4j + i is at stage
+  // i) and runs the ones in range.  The range guard runs after steps 63,
+  // 127, ...: a step there is at stage 3.
+  static_assert(kStages == 4 && kGuardSteps % kStages == 0, "four steps, one per stage");
+  {
+    const int lo = it, hi = w.m_late;
+    for (int i0 = lo & ~(kStages - 1); i0 < hi; i0 += kStages) {
+      if (i0 >= lo) plain_step(i0, 0);
+      if (i0 + 1 >= lo && i0 + 1 < hi) plain_step(i0 + 1, 1);
+      if (i0 + 2 >= lo && i0 + 2 < hi) plain_step(i0 + 2, 2);
+      if (i0 + 3 >= lo && i0 + 3 < hi) {
+        plain_step(i0 + 3, 3);
+        if ((i0 + 3) % kGuardSteps == kGuardSteps - 1) guard_planes(acc, w.lane, zref, lsum);
+      }
+    }
+    it = max(lo, hi);
   }
-  for (; it < w.m_late; ++it) {
-    next_stage(it);
-    attn_step<false>(st[it % kStages], qf[0], w.lane, w.rc.g, rowf[0], 0u, zref, lsum, acc, job, w.plan);
-    if (it % kGuardSteps == kGuardSteps - 1) guard_planes(acc, w.lane, zref, lsum);
-  }
-  for (; it < w.n_st; ++it) {
-    next_stage(it);
-    attn_step<true>(st[it % kStages], qf[0], w.lane, w.rc.g, rowf[0], key_mask(w.tb, w.tw, it, w.rc), zref, lsum,
-                    acc, job, w.plan);
-  }
+  for (; it < w.n_st; ++it) masked_step(it);
 
   // ---- epilogue: recombine the digit planes, scale by cap / (Xmax * l), store.
   // Output register i of tile nt is row 4g + i, channel 16nt + lane%16.
