@@ -73,12 +73,10 @@ constexpr float kTiny = 0x1p-60f;
 // The per-row reference: raised to ceil(row max) + kRefHeadroom when the
 // row's maximum passes it.  The two int32 planes of a row hold the value
 // 256 hi + lo; it is divided by 2^d with floor, exactly, in stages of at most
-// kStageShift bits (the carried remainder << 8 stays in int32).  With
-// |256 hi + lo| < 2^40, two stages (kMaxShift bits) take any value to 0 or -1,
-// which is what any larger floor shift gives.
+// 8 bits (floor divisions compose).  With |256 hi + lo| < 2^40, kMaxShift bits
+// take any value to 0 or -1, which is what any larger floor shift gives.
 constexpr float kRefHeadroom = 1.f;
-constexpr int kStageShift = 22;
-constexpr float kMaxShift = 2.f * kStageShift;
+constexpr float kMaxShift = 40.f;
 // log2(v_scale) enters the reference as log2(max(v_scale, kVsFloor)): a zero
 // v_scale (the KV writer's scale of an all-zero V row) still sets a finite
 // reference, and every e = exp2(score * log2(e) - zref) stays below 2^63
@@ -326,20 +324,17 @@ __device__ inline v4i read_v(const LdsAddr& A, int st, int nt) {
 }
 
 // Register i of both planes (one accumulator row per 16 lanes) becomes
-// floor((256 hi + lo) / 2^d), exactly, for 0 <= d <= kStageShift: hi keeps
-// its high part and its low d bits move down into lo.  For d >= 1 the sum
-// lo + 256 (hi mod 2^d) is halved first (256 (hi mod 2^d) is even, so
-// floor(lo / 2) + 128 (hi mod 2^d) is the exact half, floored), which keeps
-// every intermediate below 2^31 for any int32 hi and lo; then it is shifted
-// by the remaining d - 1 bits.
+// floor((256 hi + lo) / 2^d), exactly, for 0 <= d <= 8: hi keeps its high
+// part and its low d bits move down into lo.  256 (hi mod 2^d) / 2^d is a
+// whole number, so floor((lo + 256 (hi mod 2^d)) / 2^d) = (lo >> d) + (hi mod
+// 2^d) 2^(8-d), and that sum stays in int32 for any int32 hi and lo.
 __device__ inline void shift_planes(v4i (&acc)[2][16], int i, int d) {
   const int m = (1 << d) - 1;
-  const int s1 = min(d, 1);
 #pragma unroll
   for (int nt = 0; nt < 16; ++nt) {
     const int hi = acc[1][nt][i], lo = acc[0][nt][i];
     acc[1][nt][i] = hi >> d;
-    acc[0][nt][i] = (int)((uint32_t)(lo >> s1) + ((uint32_t)(hi & m) << (8 - s1))) >> (d - s1);
+    acc[0][nt][i] = (int)((uint32_t)(lo >> d) + ((uint32_t)(hi & m) << (8 - d)));
   }
 }
 
@@ -433,9 +428,12 @@ __device__ __attribute__((always_inline)) inline void attn_step(const LdsAddr& A
       for (int i = 0; i < 4; ++i) {
         const int di = __shfl(dl, 4 * g + i);  // shift of accumulator row 4g + i
         if (__builtin_amdgcn_ballot_w64(di != 0) != 0) {
-          const int d1 = min(di, kStageShift), d2 = di - d1;
-          shift_planes(acc, i, d1);
-          if (__builtin_amdgcn_ballot_w64(d2 != 0) != 0) shift_planes(acc, i, d2);
+          int rem = di;  // in stages of at most 8 bits
+          do {
+            const int dd = min(rem, 8);
+            shift_planes(acc, i, dd);
+            rem -= dd;
+          } while (__builtin_amdgcn_ballot_w64(rem != 0) != 0);
         }
       }
     }
