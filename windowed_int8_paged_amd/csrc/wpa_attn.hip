@@ -57,7 +57,7 @@ constexpr int kStepKeys = 64;                 // keys per step (four pages)
 constexpr int kStage = kStepKeys * kHeadDim;  // bytes of one staged K or V tile
 constexpr int kWaves = 8;                     // waves per workgroup
 constexpr int kStages = 4;                    // LDS ring depth
-constexpr int kLead = kStages - 1;            // a step's copies are issued this many steps before it runs
+constexpr int kLead = 2;                      // a step's copies are issued this many steps before it runs
 constexpr int kCopies = 5;                    // copies per wave and step (4 x 1 KB rows + 1 scale row)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kKeysPerGroup = 4;              // keys (rows) of one 1 KB copy group
@@ -675,31 +675,34 @@ __global__ __launch_bounds__(512, 1) void prefill_attn_kernel(AttnArgs a, const 
   for (int pl = 0; pl < 2; ++pl)
 #pragma unroll
     for (int nt = 0; nt < 16; ++nt) acc[pl][nt] = v4i{0, 0, 0, 0};
-  // every wave runs n_st steps with one barrier each; only which steps are
-  // masked differs between the waves.  Before step `it`, the wave's own
-  // copies of that step are complete once at most the copies of the later
-  // steps already issued (up to kLead - 1 of them) are in flight; the
-  // barrier then makes every wave's copies visible and frees the stage read
-  // in the previous step, which takes the copies kLead steps ahead.
-  static_assert(kLead == 3, "the waits below count two later steps");
+  // every wave runs the same n_st steps; only which steps are masked differs
+  // between the waves.  A barrier comes before every even step: there each
+  // wave waits for all its copies in flight (those of this step and the
+  // next, issued in the two steps before), and the barrier makes every
+  // wave's copies visible for both steps.  It also means every wave has
+  // finished the two steps before, so their stages are free: the copies a
+  // step issues (kLead = 2 steps ahead) go into the stage read two steps
+  // earlier, and a ring of four stages holds the two steps being read and
+  // the two being filled.
+  static_assert(kLead == 2 && kStages == 4, "a barrier every second step");
   CopyJob job;
-  // `sj` = (it + kLead) % kStages, the stage that takes the copies issued in step it
-  auto next_stage = [&](int it, int sj) __attribute__((always_inline)) {
-    const int later = w.n_st - 1 - it;
-    if (later >= 2) wait_vm<2 * kCopies>();
-    else if (later == 1) wait_vm<kCopies>();
-    else wait_vm<0>();
-    __syncthreads();
+  // `sj` = (it + kLead) % kStages, the stage that takes the copies issued in
+  // step it; `even`: it is even, the step starts with a barrier
+  auto next_stage = [&](int it, int sj, bool even) __attribute__((always_inline)) {
+    if (even) {
+      wait_vm<0>();
+      __syncthreads();
+    }
     job = make_job(it + kLead < w.n_st, ring, sj, a, w.plan, w.page_bytes, w.scale_stride, pg1);
     pg1 = pg2;
     pg2 = step_page(pt, w.tb, it + kLead + 2, w.plan.page);
   };
   auto plain_step = [&](int it, int st) __attribute__((always_inline)) {
-    next_stage(it, (st + kLead) % kStages);
+    next_stage(it, (st + kLead) % kStages, st % 2 == 0);
     attn_step<false>(A, st, qf[0], w.lane, w.rc.g, rowf[0], 0u, zref, lsum, acc, job, w.plan);
   };
   auto masked_step = [&](int it) __attribute__((always_inline)) {
-    next_stage(it, (it + kLead) % kStages);
+    next_stage(it, (it + kLead) % kStages, it % 2 == 0);
     attn_step<true>(A, it % kStages, qf[0], w.lane, w.rc.g, rowf[0], key_mask(w.tb, w.tw, it, w.rc), zref, lsum,
                     acc, job, w.plan);
   };
