@@ -68,6 +68,23 @@ def test_chunks_equal_one_call_bitwise(W, S, hq, hkv):
         assert torch.equal(torch.cat(parts), one)
 
 
+def test_long_call_in_xcd_runs_equals_chunks_bitwise():
+    """A call long enough that each XCD takes a contiguous run of tile groups
+    (512 groups per KV head) against two chunks short enough to take every
+    other group: the order of the groups over the chip must not change a bit."""
+    import windowed_int8_paged_amd as wpa
+    case = workloads.make_case(n_tokens=16384, n_q_heads=16, n_kv_heads=4, window_blocks=256, sink_blocks=1,
+                               seed=41)
+    dev = upload(case)
+    _say("one 16384-row call (XCD runs) vs two 8192-row chunks")
+    q_i8, q_scale = wpa.quantize_q_rows(dev["q_bf16"])
+    one = wpa.prefill_attn_i8(q_i8, q_scale, dev["k_pool"], dev["v_pool"], dev["k_scale"], dev["v_scale"],
+                              dev["page_table"], case.window_blocks, case.sink_blocks, case.softmax_scale,
+                              out_dtype=torch.bfloat16)
+    parts = [run_chunk(case, dev, a, 8192, torch.bfloat16) for a in (0, 8192)]
+    assert torch.equal(torch.cat(parts), one)
+
+
 @pytest.mark.parametrize("n_total,q_start,hq,hkv,W,S,seed", [
     (500, 320, 8, 2, 4, 2, 31),     # ragged chunk at the end, windowed
     (500, 160, 4, 1, 0, 0, 32),     # full causal, chunk in the middle
