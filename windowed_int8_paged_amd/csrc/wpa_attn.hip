@@ -393,6 +393,11 @@ __device__ __attribute__((always_inline)) inline void attn_step(const LdsAddr& A
                                  const DmaPlan& plan) {
   v4i s[4];
   qk_step<8>(A, st, qf, s);
+  // The weights run at a raised wave priority, the products at the normal
+  // one: where the two waves of a SIMD are in different phases, the arbiter
+  // issues the vector work first.  Measured 0.5-1% faster at 32k, 64k and
+  // 16k full causal and about 4% at 4k, with the same bits.
+  __builtin_amdgcn_s_setprio(1);
   const uint32_t sc = (uint32_t)(st * kScStage);
   // log2(v_scale) of the step's 64 keys, one per lane, into the spare scale
   // slots (every wave writes the same values)
@@ -482,6 +487,7 @@ __device__ __attribute__((always_inline)) inline void attn_step(const LdsAddr& A
     dig[1][t] = (int)__builtin_amdgcn_perm(w23, w01, 0x07050301u);                 // high digit
   }
 
+  __builtin_amdgcn_s_setprio(0);
   // V operand (see read_v): reads run two column tiles ahead of their
   // products (see qk_step)
   constexpr int DV = 2;
