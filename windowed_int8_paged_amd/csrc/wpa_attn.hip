@@ -36,10 +36,10 @@
 //     a factor 4 of it.  P codes depend only on ratios inside their block, so
 //     the reference does not change them.
 //   * K and V pages go global -> LDS by asynchronous LDS DMA into row-major
-//     XOR-swizzled tiles, in a ring of four stages filled three steps ahead.
-//     Each wave issues five copies per step (one page of K or of V and its
-//     scales), spread among its PV products, so a page is fetched once for
-//     all eight waves.  LDS fragment reads are software-pipelined ahead of
+//     XOR-swizzled tiles, in a ring of four stages filled two steps ahead,
+//     with one workgroup barrier every second step.  Each wave issues five
+//     copies per step (one page of K or of V and its scales), spread among
+//     its PV products, so a page is fetched once for all eight waves.  LDS fragment reads are software-pipelined ahead of
 //     their matrix products; V operands are gathered with the transposing
 //     read ds_read_b64_tr_b8.  The unmasked steps run with their ring stage
 //     known, so every LDS read is a register holding the lane's address plus
