@@ -236,7 +236,8 @@ wpa_status wpa_kv_write_i8(const void* k, const void* v, wpa_dtype dtype, int n_
  *                  entry reads a wrong page, never outside the pool).
  *   seq_lens       [batch] int32, device; a length above 16*max_blocks is
  *                  taken as 16*max_blocks, and a length <= 0 gives a zero row.
- *   n_q_heads / n_kv_heads must be at most 16.
+ *   n_q_heads / n_kv_heads: any; up to 16 query heads of a KV head share
+ *                  each K and V row load (more take one load per 16).
  *   workspace      device scratch of at least wpa_decode_workspace_bytes(...)
  *                  bytes, 16-byte aligned, owned by the caller; its contents
  *                  on entry do not matter.  Calls that share a workspace
@@ -246,8 +247,8 @@ wpa_status wpa_kv_write_i8(const void* k, const void* v, wpa_dtype dtype, int n_
  * Errors: NULL pointer -> WPA_ERR_NULL; batch < 0, heads <= 0,
  * n_q_heads % n_kv_heads != 0, max_blocks <= 0, n_pool_pages <= 0,
  * sink_blocks < 0, softmax_scale not finite or <= 0, or a workspace smaller
- * than needed -> WPA_ERR_SHAPE; other dtype, misalignment or more than 16
- * query heads per KV head -> WPA_ERR_UNSUPPORTED.
+ * than needed -> WPA_ERR_SHAPE; other dtype, misalignment or a grid past
+ * 2^31 workgroups -> WPA_ERR_UNSUPPORTED.
  */
 size_t wpa_decode_workspace_bytes(int batch, int n_q_heads, int max_blocks, int window_blocks,
                                   int sink_blocks);

@@ -205,7 +205,8 @@ def test_decode_rejects_invalid_arguments(lib):
     assert d(scale=0.0) == SHAPE
     assert d(ws_bytes=need - 1) == SHAPE
     assert d(dtype=9) == UNSUP
-    assert d(hq=34, hkv=2) == UNSUP       # 17 query heads per KV head
+    # 17 query heads per KV head are accepted (two groups of heads); batch 0 launches nothing
+    assert d(hq=34, hkv=2, batch=0, q=None, lens=None, ws=None, out=None) == OK
     assert d(q=None) == NULL
     assert d(lens=None) == NULL
     assert d(ws=None) == NULL
@@ -230,7 +231,7 @@ def test_decode_noalloc_rejects_invalid_arguments(lib):
     assert d(hq=6, hkv=4) == SHAPE
     assert d(scale=float("nan")) == SHAPE
     assert d(dtype=9) == UNSUP
-    assert d(hq=34, hkv=2) == UNSUP
+    assert d(hq=34, hkv=2, batch=0, q=None, lens=None, out=None) == OK
     assert d(q=None) == NULL
     assert d(out=None) == NULL
     assert d(batch=0, q=None, lens=None, out=None) == OK

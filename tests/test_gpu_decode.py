@@ -58,6 +58,8 @@ def check_batch(d, out, label, seqs=None):
     ([90, 600], 6, 2, 5, 1, 56),                           # 3 heads: a partly filled (head, page) row tile
     ([129, 520], 16, 2, 6, 0, 57),                         # 8 heads: two row tiles of the PV operand
     ([64, 400], 10, 2, 0, 0, 58),                          # 5 heads: two row tiles, the second with one head
+    ([50, 700], 32, 1, 4, 1, 59),                          # 32 query heads per KV head: two groups of 16
+    ([90, 400], 40, 2, 3, 0, 60),                          # 20 per KV head: a group of 16 and one of 4
 ])
 def test_decode_parity(lens, hq, hkv, W, S, seed):
     d = poison_unattended_blocks(workloads.make_decode_batch(lens, hq, hkv, W, S, seed=seed))

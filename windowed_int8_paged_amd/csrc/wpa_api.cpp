@@ -181,13 +181,13 @@ wpa_status decode_check(const int8_t* q_i8, const float* q_scale, const int8_t* 
   if (max_blocks <= 0 || n_pool_pages <= 0 || sink_blocks < 0) return WPA_ERR_SHAPE;
   if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return WPA_ERR_SHAPE;
   if (out_dtype != WPA_BF16 && out_dtype != WPA_F32) return WPA_ERR_UNSUPPORTED;
-  if (n_q_heads / n_kv_heads > wpa::kMaxDecodeG) return WPA_ERR_UNSUPPORTED;
   if (batch == 0) return WPA_OK;
   if (!q_i8 || !q_scale || !k_pool || !v_pool || !k_scale || !v_scale || !page_tables || !seq_lens || !out)
     return WPA_ERR_NULL;
   if (!aligned16(q_i8) || !aligned16(k_pool) || !aligned16(v_pool)) return WPA_ERR_UNSUPPORTED;
   const long splits = wpa::decode_splits(max_blocks, window_blocks, sink_blocks);
-  if ((long)batch * n_kv_heads * splits > 0x7fffffffL || (long)batch * n_q_heads > 0x7fffffffL)
+  const long head_groups = (n_q_heads / n_kv_heads + wpa::kMaxDecodeG - 1) / wpa::kMaxDecodeG;
+  if ((long)batch * n_kv_heads * head_groups * splits > 0x7fffffffL || (long)batch * n_q_heads > 0x7fffffffL)
     return WPA_ERR_UNSUPPORTED;
   (void)window_blocks;
   return WPA_OK;

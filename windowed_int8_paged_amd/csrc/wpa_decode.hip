@@ -12,8 +12,9 @@
 // full causal attention).
 //
 // Design
-//   * A workgroup takes one (sequence, KV head, split): the G <= 16 query heads
-//     of the KV head share every K and V row it loads.  A split is 8 pages (128
+//   * A workgroup takes one (sequence, KV head, split) and up to 16 query
+//     heads of the KV head, which share every K and V row it loads; a KV head
+//     with more query heads takes one workgroup per group of 16.  A split is 8 pages (128
 //     keys) of the sequence's key list, so short batches still spread over
 //     the chip; a second launch combines the splits.
 //   * The P codes of a block depend only on the ratios of P*v_scale inside the
@@ -64,10 +65,13 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   int u = blockIdx.x;
   const int sp = u % a.n_splits;
   u /= a.n_splits;
+  const int hgi = u % a.n_hg;  // which group of kMaxDecodeG query heads of the KV head
+  u /= a.n_hg;
   const int kvh = u % a.n_kv_heads;
   const int b = u / a.n_kv_heads;
-  const int G = a.G;
-  const long head_row0 = (long)b * a.n_q_heads + (long)kvh * G;  // Q / ws row of head 0 of this KV head
+  const int G = min(kMaxDecodeG, a.G - kMaxDecodeG * hgi);  // query heads of this workgroup
+  // Q / ws row of the workgroup's first head
+  const long head_row0 = (long)b * a.n_q_heads + (long)kvh * a.G + (long)kMaxDecodeG * hgi;
   float* ws = a.ws + head_row0 * a.n_splits * kWsRow;
 
   // the query position; lengths beyond the page table are clamped to it
@@ -348,7 +352,8 @@ hipError_t launch_decode(const DecodeArgs& args_in, bool out_bf16, hipStream_t s
   a.G = a.n_q_heads / a.n_kv_heads;
   a.row_mul = a.softmax_scale * kLog2eD;
   a.n_splits = decode_splits(a.max_blocks, a.window_blocks, a.sink_blocks);
-  const unsigned grid = (unsigned)((long)a.batch * a.n_kv_heads * a.n_splits);
+  a.n_hg = (a.G + kMaxDecodeG - 1) / kMaxDecodeG;
+  const unsigned grid = (unsigned)((long)a.batch * a.n_kv_heads * a.n_hg * a.n_splits);
   hipLaunchKernelGGL(decode_split_kernel, dim3(grid), dim3(256), 0, stream, a);
   const unsigned rows = (unsigned)((long)a.batch * a.n_q_heads);
   if (out_bf16) hipLaunchKernelGGL(decode_combine_kernel<true>, dim3(rows), dim3(256), 0, stream, a);

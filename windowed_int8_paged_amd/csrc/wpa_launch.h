@@ -31,7 +31,7 @@ struct AttnArgs {
 };
 
 // Split-KV decode (wpa_decode.hip).
-constexpr int kMaxDecodeG = 16;  // query heads per KV head
+constexpr int kMaxDecodeG = 16;  // query heads of one KV head per workgroup
 constexpr int kWsRow = 260;      // floats per (sequence, head, split): O[256], Z, l, 2 pad (16-byte rows)
 struct DecodeArgs {
   const int8_t* q_i8;
@@ -48,7 +48,7 @@ struct DecodeArgs {
   int window_blocks, sink_blocks;
   float softmax_scale;
   // filled in by the launcher
-  int G, n_splits;
+  int G, n_splits, n_hg;  // n_hg groups of up to kMaxDecodeG query heads per KV head
   float row_mul;
 };
 int decode_splits(int max_blocks, int window_blocks, int sink_blocks);
