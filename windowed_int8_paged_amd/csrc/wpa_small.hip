@@ -12,8 +12,6 @@
 
 namespace wpa {
 
-typedef unsigned v2u __attribute__((ext_vector_type(2)));
-
 // Eight consecutive channels of a 256-channel row held by one of 32 lanes.
 template <bool BF16>
 __device__ inline void load8(const void* __restrict__ x, long row, int sub, float (&v)[8]) {
@@ -68,10 +66,8 @@ __global__ __launch_bounds__(256) void quantize_q_rows_kernel(const void* __rest
     float scale;
     const uint2 codes = quant8(v[i], scale);
     if (row < n_rows) {
-      // non-temporal stores: 16% faster at 32k x 16 heads, where the same hint
-      // on the loads, or on the KV writer's scattered pool rows, was slower
-      __builtin_nontemporal_store(v2u{codes.x, codes.y}, reinterpret_cast<v2u*>(q_i8) + row * 32 + sub);
-      if (sub == 0) __builtin_nontemporal_store(scale, q_scale + row);
+      reinterpret_cast<uint2*>(q_i8)[row * 32 + sub] = codes;
+      if (sub == 0) q_scale[row] = scale;
     }
   }
 }
