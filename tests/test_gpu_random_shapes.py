@@ -1,7 +1,7 @@
-"""Sixteen seeded random shapes through every prefill entry point (C ABI), each checked
-against the oracle at the acceptance bars.
+"""Seeded random shapes through every prefill entry point (C ABI), and seeded random
+decode batches, each checked against the oracle at the acceptance bars.
 
-The shapes are drawn once from a fixed seed: lengths from 1 to 1500 tokens
+The prefill shapes are drawn from fixed seeds (16 from one, 60 from another): lengths from 1 to 1500 tokens
 (ragged tails included), 1 to 8 query heads per KV head, 1 to 4 KV heads,
 window and sink blocks covering full causal, narrow and over-wide windows,
 and a chunk start on a random page boundary.  For each shape the int8-Q path,
@@ -38,7 +38,7 @@ def _shapes(n_cases=16, seed=20261202):
     return out
 
 
-@pytest.mark.parametrize("n,hq,hkv,W,S,q_start,seed", _shapes())
+@pytest.mark.parametrize("n,hq,hkv,W,S,q_start,seed", _shapes() + _shapes(60, 777))
 def test_random_shape(n, hq, hkv, W, S, q_start, seed):
     import windowed_int8_paged_amd as wpa
     case = workloads.make_case(n_tokens=n, n_q_heads=hq, n_kv_heads=hkv, window_blocks=W, sink_blocks=S,
@@ -63,3 +63,33 @@ def test_random_shape(n, hq, hkv, W, S, q_start, seed):
     rng = np.random.default_rng(seed)
     tiles = sorted({0, nt - 1, q_start // 16, *rng.integers(0, nt, size=3).tolist()})
     check_parity(case, full, tiles=tiles, label=f"random n={n}")
+
+
+def _decode_batches(n_cases=40, seed=778):
+    """Ragged batches of 1-4 sequences of 1-3000 tokens, 1-20 query heads per KV head,
+    1-4 KV heads, full causal or a 1-23-block window, 0-3 sink blocks."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n_cases):
+        hkv = int(rng.integers(1, 5))
+        g = int(rng.integers(1, 21))
+        lens = sorted(int(x) for x in rng.integers(1, 3001, size=int(rng.integers(1, 5))))
+        w = int(rng.choice([0, int(rng.integers(1, 24))]))
+        s = int(rng.integers(0, 4))
+        out.append((lens, g * hkv, hkv, w, s, int(rng.integers(0, 2**31))))
+    return out
+
+
+@pytest.mark.parametrize("lens,hq,hkv,W,S,seed", _decode_batches())
+def test_random_decode_batch(lens, hq, hkv, W, S, seed):
+    """Every sequence's row against the prefill oracle's row t (bf16 output equal to the RNE
+    of the fp32 one); unattended blocks point at the NaN-scaled page 0."""
+    from gpu_util import poison_unattended_blocks
+    from test_gpu_decode import check_batch, run_decode, upload_batch
+    d = poison_unattended_blocks(workloads.make_decode_batch(lens, hq, hkv, W, S, seed=seed))
+    dev = upload_batch(d)
+    print(f"random decode lens={lens} hq={hq} hkv={hkv} W={W} S={S}", flush=True)
+    o32 = run_decode(d, dev, torch.float32)
+    check_batch(d, o32, f"random decode {lens}")
+    o16 = run_decode(d, dev, torch.bfloat16)
+    assert torch.equal(o16, o32.to(torch.bfloat16))
