@@ -32,14 +32,17 @@ COUNTERS_FILE = os.path.join(ROOT, "profiles", "prefill_attn_32k_counters.json")
 
 
 def kernel_source_hash() -> str:
-    """Hash of the attention kernels' code with comments and blank space removed, so the
-    recorded traffic counters stay attached to a build until its code changes."""
+    """Hash of the attention kernels' code with comments and blank space removed, and of
+    the compiler flags they are built with, so the recorded traffic counters stay attached
+    to a build until its code changes."""
+    from windowed_int8_paged_amd import build as wpa_build
     h = hashlib.sha256()
     for p in ATTN_KERNEL_SOURCES:
         text = open(os.path.join(ROOT, p)).read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
         text = re.sub(r"//[^\n]*", " ", text)
         h.update(" ".join(text.split()).encode())
+    h.update(" ".join(wpa_build.HIP_FLAGS + wpa_build.SOURCE_FLAGS.get("wpa_attn.hip", [])).encode())
     return h.hexdigest()[:16]
 
 

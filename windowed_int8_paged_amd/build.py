@@ -20,6 +20,11 @@ SOURCES = ["wpa_api.cpp", "wpa_small.hip", "wpa_attn.hip", "wpa_decode.hip"]
 # that it does not know the feature; that is harmless).
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Per-source flags.  The attention kernels are scheduled for instruction-level
+# parallelism: the same code and bits, about 0.8% faster at 32k and 16k full
+# causal than the default strategy (the register-minimizing one was 3-4%
+# slower).
+SOURCE_FLAGS = {"wpa_attn.hip": ["-mllvm", "--amdgpu-sched-strategy=max-ilp"]}
 
 
 def hipcc() -> str:
@@ -47,7 +52,7 @@ def build(verbose: bool = False, extra_flags=()) -> str:
     for src in SOURCES:
         obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
         lang = ["-x", "hip"] if src.endswith(".cpp") else []
-        jobs.append((obj, [cc, *HIP_FLAGS, *extra_flags, *inc, *lang, "-c",
+        jobs.append((obj, [cc, *HIP_FLAGS, *SOURCE_FLAGS.get(src, []), *extra_flags, *inc, *lang, "-c",
                            os.path.join(CSRC, src), "-o", obj]))
     with ThreadPoolExecutor(max_workers=len(jobs)) as ex:
         outs = list(ex.map(lambda j: _run(j[1]), jobs))
